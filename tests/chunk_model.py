@@ -1,0 +1,86 @@
+"""numpy fp64 model of the chunked (UT / WY) form that the HIP kernels use.
+
+Not the oracle and not GPU code: a second CPU model that checks the algebra
+of the chunk form against the token-by-token oracle, so that a kernel bug and
+an algebra bug can be told apart.
+
+Within a chunk of c tokens with chunk-local cumulative log-decays
+Gam_t = sum_{i<=t} g_i (per channel):
+    K_L  rows exp(Gam_t) * k_t            Kt  rows exp(Gam_c - Gam_t) * k_t
+    G_ti = sum_ch k_t,ch k_i,ch exp(Gam_t,ch - Gam_i,ch)      (t > i)
+    A    = (I + diag(beta) tril(G, -1))^-1 diag(beta)
+    W = A K_L,  U = A V
+    [T | S] <- diag(exp(Gam_c)) [T | S] + Kt^T ([0 | U] - W [T | S])
+Families without erasure drop W and use U = diag(beta) V.
+Outputs of a chunk read from S0:
+    X = A (V - K_L S0);   o_t = S0^T (exp(Gam_t) * q_t) + sum_{i<=t} ((exp(Gam_t - Gam_i) * q_t) . k_i) x_i
+"""
+import numpy as np
+
+DELTA = ("deltanet", "gdn", "kda")
+
+
+def _logdecay(fam, g, gamma, n, dk):
+    if fam in ("linear", "deltanet"):
+        return np.zeros((n, dk))
+    if fam == "retnet":
+        return np.full((n, dk), np.log(gamma))
+    if fam in ("mamba2", "gdn"):
+        return np.repeat(np.asarray(g, dtype=np.float64).reshape(n, 1), dk, axis=1)
+    return np.asarray(g, dtype=np.float64).reshape(n, dk)
+
+
+def _chunk_factors(fam, K, V, Gm, b):
+    L, dk = K.shape
+    Kl = np.exp(Gm) * K
+    Kt = np.exp(Gm[-1] - Gm) * K
+    if fam in DELTA:
+        G = np.zeros((L, L))
+        for t in range(L):
+            for i in range(t):
+                G[t, i] = np.sum(K[t] * K[i] * np.exp(Gm[t] - Gm[i]))
+        A = np.linalg.solve(np.eye(L) + np.diag(b) @ G, np.diag(b))
+        return Kl, Kt, A
+    return Kl, Kt, np.diag(b)
+
+
+def chunk_pair(fam, k, v, g=None, beta=None, gamma=1.0, c=64):
+    k, v = np.asarray(k, np.float64), np.asarray(v, np.float64)
+    n, dk = k.shape
+    dv = v.shape[1]
+    lg = _logdecay(fam, g, gamma, n, dk)
+    bb = np.ones(n) if beta is None or fam not in DELTA else np.asarray(beta, np.float64)
+    X = np.concatenate([np.eye(dk), np.zeros((dk, dv))], axis=1)
+    for s in range(0, n, c):
+        e = min(n, s + c)
+        K, V = k[s:e], v[s:e]
+        Gm = np.cumsum(lg[s:e], axis=0)
+        Kl, Kt, A = _chunk_factors(fam, K, V, Gm, bb[s:e])
+        Y = np.concatenate([np.zeros((e - s, dk)), A @ V], axis=1)
+        M = A @ Kl @ X if fam in DELTA else 0.0
+        X = np.exp(Gm[-1])[:, None] * X + Kt.T @ (Y - M)
+    return X[:, :dk], X[:, dk:]
+
+
+def chunk_run(fam, q, k, v, g=None, beta=None, gamma=1.0, S0=None, c=64):
+    """Outputs and final state of the recurrence read in chunks from S0."""
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+    n, dk = k.shape
+    dv = v.shape[1]
+    lg = _logdecay(fam, g, gamma, n, dk)
+    bb = np.ones(n) if beta is None or fam not in DELTA else np.asarray(beta, np.float64)
+    S = np.zeros((dk, dv)) if S0 is None else np.asarray(S0, np.float64).copy()
+    O = np.zeros((n, dv))
+    for s in range(0, n, c):
+        e = min(n, s + c)
+        K, V, Q = k[s:e], v[s:e], q[s:e]
+        Gm = np.cumsum(lg[s:e], axis=0)
+        Kl, Kt, A = _chunk_factors(fam, K, V, Gm, bb[s:e])
+        X = A @ (V - Kl @ S) if fam in DELTA else A @ V
+        for t in range(e - s):
+            o = S.T @ (np.exp(Gm[t]) * Q[t])
+            for i in range(t + 1):
+                o += np.dot(np.exp(Gm[t] - Gm[i]) * Q[t], K[i]) * X[i]
+            O[s + t] = o
+        S = np.exp(Gm[-1])[:, None] * S + Kt.T @ X
+    return S, O

@@ -1,0 +1,46 @@
+"""The chunked UT/WY form used by the kernels equals the token-by-token oracle
+(fp64, CPU).  Chunk sizes 1, 8, 64 and lengths with ragged chunk tails."""
+import numpy as np
+import pytest
+
+import oracle
+from chunk_model import chunk_pair, chunk_run
+
+FAMS = ["linear", "retnet", "mamba2", "gla", "deltanet", "gdn", "kda"]
+
+
+def _inputs(rng, fam, n, dk, dv):
+    k = rng.normal(size=(n, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    q = rng.normal(size=(n, dk))
+    v = rng.normal(size=(n, dv))
+    g = None
+    if fam in ("mamba2", "gdn"):
+        g = -np.log1p(np.exp(rng.normal(-3, 0.5, size=n)))
+    elif fam in ("gla", "kda"):
+        g = -np.log1p(np.exp(rng.normal(-4, 1.0, size=(n, dk))))
+    beta = 1 / (1 + np.exp(-rng.normal(size=n))) if fam in ("deltanet", "gdn", "kda") else None
+    return q, k, v, g, beta, (0.97 if fam == "retnet" else 1.0)
+
+
+@pytest.mark.parametrize("fam", FAMS)
+@pytest.mark.parametrize("c", [1, 8, 64])
+def test_chunk_pair_matches_oracle(fam, c):
+    rng = np.random.default_rng(50 + FAMS.index(fam) * 3 + c)
+    for n in (1, 9, 64, 65, 150):
+        q, k, v, g, beta, gamma = _inputs(rng, fam, n, 8, 6)
+        T, S = oracle.pair(fam, k, v, g, beta, gamma)
+        Tc, Sc = chunk_pair(fam, k, v, g, beta, gamma, c)
+        assert oracle.rel_fro(Tc, T) < 1e-11 and oracle.rel_fro(Sc, S) < 1e-11, (n, c)
+
+
+@pytest.mark.parametrize("fam", FAMS)
+@pytest.mark.parametrize("c", [8, 64])
+def test_chunk_outputs_match_oracle(fam, c):
+    rng = np.random.default_rng(90 + FAMS.index(fam))
+    q, k, v, g, beta, gamma = _inputs(rng, fam, 77, 8, 6)
+    S0 = rng.normal(size=(8, 6))
+    S, O = oracle.run(fam, q, k, v, g, beta, gamma, S0)
+    Sc, Oc = chunk_run(fam, q, k, v, g, beta, gamma, S0, c)
+    assert oracle.rel_fro(Sc, S) < 1e-11
+    assert oracle.rel_fro(Oc, O) < 1e-11
