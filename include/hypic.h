@@ -1,0 +1,187 @@
+/*
+ * hypic.h -- C ABI of libhypic: segment state caching for the linear-attention
+ * layers of hybrid models, on AMD Instinct MI355X (gfx950).
+ *
+ * The method (HYPIC; codernav.top article, section "linear layers: caching
+ * the segment-accumulated transition operator"; xix.ai article, paragraph on
+ * linear layers):  a linear-attention layer keeps one state S (dk x dv) per
+ * head and every token t updates it as
+ *        S_t = A_t S_{t-1} + beta_t k_t v_t^T,      o_t = S_t^T q_t
+ * with a family-specific transition A_t.  For each prompt segment C the
+ * library caches the pair (T_C, S(C|0)): T_C is the ordered product of the
+ * segment's transitions (later tokens on the left) and S(C|0) the segment's
+ * final state read from a zero state.  Any request's state is then assembled
+ * with the composition law  S(C1.C2) = T(C2) S(C1) + S(C2).  The first w
+ * tokens of every internal segment (the seam window; codernav.top article,
+ * section on full-attention layers and seam windows, w = 8 by default) are
+ * kept out of the cache and advanced token by token at reuse, emitting their
+ * outputs o_t.
+ *
+ * Transitions (state S is dk x dv; g is the log-gate, decay = exp(g)):
+ *   HYPIC_LINEAR    A = I                                  beta = 1
+ *   HYPIC_RETNET    A = gamma I   (gamma per chain)        beta = 1
+ *   HYPIC_MAMBA2    A = exp(g_t) I   (scalar g)            beta = 1
+ *   HYPIC_GLA       A = diag(exp(g_t))   (g_t in R^dk)     beta = 1
+ *   HYPIC_DELTANET  A = I - beta_t k_t k_t^T
+ *   HYPIC_GDN       A = exp(g_t) (I - beta_t k_t k_t^T)
+ *   HYPIC_KDA       A = (I - beta_t k_t k_t^T) diag(exp(g_t))   (decay, then erase)
+ *
+ * Conventions shared by every call
+ *   - A "chain" is one (layer, head) of one request; n_chains chains share
+ *     every token index.  Token tensors are token-major:
+ *       q, k: x[t*tok_stride + c*chain_stride + i], i < dk
+ *       v:    x[t*tok_stride + c*chain_stride + j], j < dv
+ *       g:    g[t*g_tok_stride + c*g_chain_stride (+ i for GLA/KDA)]
+ *       beta: beta[t*b_tok_stride + c*b_chain_stride]
+ *     Strides are in elements; the innermost (feature) axis is contiguous.
+ *   - q, k, v, g, beta have the layout's in_dtype (fp32 or bf16).  gamma,
+ *     T, S, states and outputs are fp32.
+ *   - dk == dv, with dk in {16, 32, 64, 128}.
+ *   - Every pointer argument named d_* is DEVICE memory the caller owns; the
+ *     library never allocates, frees or keeps device memory (a workspace, when
+ *     an op needs one, is passed in and sized by hypic_workspace_bytes).
+ *     Structs and scalar arguments are host memory, read during the call.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) with no host synchronisation.  Calls on different streams are
+ *     thread-safe.
+ *   - Errors: arguments visible on the host are validated before any HIP
+ *     call (null pointers, unknown family/dtype, dims, w, strides and 16-byte
+ *     alignment of q/k/v rows, workspace size).  A failing check returns a
+ *     negative status and enqueues nothing.  Launch failures return
+ *     HYPIC_E_DEVICE.  Device-resident contents (offsets, slot ids) are
+ *     trusted; out-of-range values there are undefined behaviour.  The detail
+ *     of the last error on the calling thread is in hypic_last_error().
+ *     On error the outputs are unspecified.
+ */
+#ifndef HYPIC_H
+#define HYPIC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum hypic_status {
+    HYPIC_OK = 0,
+    HYPIC_E_INVALID = -1,     /* bad argument (null pointer, size, stride, alignment, w) */
+    HYPIC_E_UNSUPPORTED = -2, /* valid request this build does not implement */
+    HYPIC_E_WORKSPACE = -3,   /* workspace missing or too small */
+    HYPIC_E_DEVICE = -4       /* HIP launch or runtime error */
+};
+
+enum hypic_family {
+    HYPIC_LINEAR = 0,
+    HYPIC_RETNET = 1,
+    HYPIC_MAMBA2 = 2,
+    HYPIC_GLA = 3,
+    HYPIC_DELTANET = 4,
+    HYPIC_GDN = 5,
+    HYPIC_KDA = 6
+};
+
+enum hypic_dtype { HYPIC_F32 = 0, HYPIC_BF16 = 1 };
+
+/* hypic_compose modes: left-to-right, or the associative tree scan with
+ * (T_b, S_b) o (T_a, S_a) = (T_b T_a, T_b S_a + S_b). */
+enum hypic_mode { HYPIC_SEQ = 0, HYPIC_TREE = 1 };
+
+/* hypic_workspace_bytes ops */
+enum hypic_op { HYPIC_OP_BUILD = 0, HYPIC_OP_COMPOSE_SEQ = 1, HYPIC_OP_COMPOSE_TREE = 2, HYPIC_OP_SEAM = 3 };
+
+typedef struct hypic_layout {
+    int32_t family;   /* enum hypic_family */
+    int32_t in_dtype; /* enum hypic_dtype of q, k, v, g, beta */
+    int32_t n_chains; /* chains per token index (e.g. layers x heads), >= 1 */
+    int32_t dk;       /* key / state rows */
+    int32_t dv;       /* value / state columns; must equal dk */
+} hypic_layout;
+
+typedef struct hypic_tokens {
+    const void *q;       /* [tok][chain][dk]; read only by seam advance (may be NULL for build) */
+    const void *k;       /* [tok][chain][dk] */
+    const void *v;       /* [tok][chain][dv] */
+    const void *g;       /* log-gates: [tok][chain] (MAMBA2, GDN) or [tok][chain][dk] (GLA, KDA); else NULL */
+    const void *beta;    /* [tok][chain] (DELTANET, GDN, KDA); else NULL */
+    const float *gamma;  /* [n_chains] fp32 (RETNET); else NULL */
+    int64_t tok_stride, chain_stride;     /* q, k, v */
+    int64_t g_tok_stride, g_chain_stride; /* g */
+    int64_t b_tok_stride, b_chain_stride; /* beta */
+} hypic_tokens;
+
+/* Number of fp32 values one cached T occupies for a family: 1 (LINEAR,
+ * RETNET, MAMBA2: a scalar times I), dk (GLA: a diagonal), dk*dk (DELTANET,
+ * GDN, KDA: dense, row-major).  0 for an unknown family. */
+int64_t hypic_t_elems(int32_t family, int32_t dk);
+
+/* Device workspace, in bytes, that `op` needs for n_items (segments for
+ * BUILD, requests for COMPOSE_*, items for SEAM) with max_len the longest
+ * segment (BUILD) or list (COMPOSE_*).  0 means no workspace is needed. */
+size_t hypic_workspace_bytes(const hypic_layout *L, int32_t op, int32_t n_items, int64_t max_len);
+
+/*
+ * hypic_segment_build -- the cached pair of every segment on every chain.
+ * (codernav.top, linear layers: at a segment's first prefill the system
+ * caches (T_C, S(C|0)); both depend only on the segment's own tokens.)
+ *
+ * Segment s covers tokens [d_seg_begin[s], d_seg_end[s]) of x; an empty range
+ * gives T = I, S = 0.  max_seg_len (host) bounds every segment's length.
+ * Outputs, fully overwritten:
+ *   d_T [n_seg][n_chains][hypic_t_elems(family, dk)]
+ *   d_S [n_seg][n_chains][dk][dv]
+ * d_T and d_S must not overlap the inputs.
+ */
+int hypic_segment_build(const hypic_layout *L, const hypic_tokens *x, int32_t n_seg,
+                        const int64_t *d_seg_begin, const int64_t *d_seg_end, int64_t max_seg_len,
+                        float *d_T, float *d_S, void *d_ws, size_t ws_bytes, void *stream);
+
+/*
+ * hypic_compose -- assemble request states from cached pairs
+ * (codernav.top, linear layers: reuse left-multiplies T_C, then adds S(C|0);
+ * seam windows: the linear layers advance the running state through each
+ * seam window and pass every seam token's output up).
+ *
+ * Request r walks its entries e = d_list_off[r] .. d_list_off[r+1]-1 in
+ * order.  For each entry: if seam != NULL and d_seam_begin[e] >= 0, advance
+ * the state through tokens d_seam_begin[e] .. +w-1 of `seam`, writing
+ * o_t = S_t^T q_t to d_o[((e*w + i)*n_chains + c)*dv + j]; then apply the
+ * entry's pair:  S <- T[slot] S + S[slot],  slot = d_pair_id[e].
+ *   d_T, d_S      pair cache laid out as hypic_segment_build writes it,
+ *                 slots 0 .. n_slots-1 (read only)
+ *   d_state       [n_req][n_chains][dk][dv]: in = initial state (zero for a
+ *                 fresh request), out = final state
+ *   d_o           [n_entries][w][n_chains][dv]; rows of entries without a seam
+ *                 are left untouched.  May be NULL when seam == NULL.
+ * mode HYPIC_TREE computes the same result through the associative scan
+ * (needs a workspace); HYPIC_SEQ needs none.  max_list_len bounds every
+ * request's entry count.
+ */
+int hypic_compose(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t max_list_len,
+                  const int32_t *d_list_off, const int32_t *d_pair_id, int64_t n_slots,
+                  const float *d_T, const float *d_S, const hypic_tokens *seam,
+                  const int64_t *d_seam_begin, int32_t w, float *d_state, float *d_o,
+                  void *d_ws, size_t ws_bytes, void *stream);
+
+/*
+ * hypic_seam_advance -- advance n_items independent states through w tokens
+ * each (codernav.top, seam windows: the linear layers compute the window's
+ * transition and state on the fly, advance the running state and emit each
+ * seam token's output).
+ *   d_tok_begin [n_items]: first token of each item's window in x
+ *   d_state     [n_items][n_chains][dk][dv], updated in place
+ *   d_o         [n_items][w][n_chains][dv], o_t = S_t^T q_t (post-update)
+ */
+int hypic_seam_advance(const hypic_layout *L, const hypic_tokens *x, int32_t n_items,
+                       const int64_t *d_tok_begin, int32_t w, float *d_state, float *d_o,
+                       void *stream);
+
+/* Static text for a status code. */
+const char *hypic_status_string(int status);
+/* Detail of the last failing call on this thread ("" if none). */
+const char *hypic_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HYPIC_H */

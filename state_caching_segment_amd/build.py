@@ -1,0 +1,47 @@
+"""Compile libhypic for gfx950 with hipcc into the package directory.
+
+Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
+selection disabled.  Objects go to ``_build/``; the shared library is written
+next to this file as ``libhypic.so`` so that it is loaded from the source tree.
+"""
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+OUT = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libhypic.so")
+SOURCES = ["api.cpp", "build_dense.hip", "build_diag.hip", "compose.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I", os.path.join(os.path.dirname(HERE), "include")]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(OUT, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # the host pass does not know the packed-fp32 feature; that warning is expected
+    msgs = [l for l in res.stdout.splitlines() if "packed-fp32-ops" not in l]
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n" + "\n".join(msgs))
+    if msgs:
+        sys.stderr.write("\n".join(msgs) + "\n")
+    return obj
+
+
+def build(jobs: int = 4) -> str:
+    os.makedirs(OUT, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build())

@@ -1,0 +1,236 @@
+// libhypic C ABI: argument validation, dispatch to the gfx950 kernels,
+// status reporting.  Every check that can be made on the host runs before
+// the first HIP call, so a rejected call enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/hypic.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok() {
+    g_last_error.clear();
+    return HYPIC_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int esize(int dtype) { return dtype == HYPIC_BF16 ? 2 : 4; }
+
+// Padded state size the kernels are instantiated for.
+int padded_d(int dk) { return dk <= 32 ? 32 : dk; }
+
+int check_layout(const hypic_layout *L) {
+    if (!L) return fail(HYPIC_E_INVALID, "layout is NULL");
+    if (L->family < HYPIC_LINEAR || L->family > HYPIC_KDA) return fail(HYPIC_E_INVALID, "unknown family %d", L->family);
+    if (L->in_dtype != HYPIC_F32 && L->in_dtype != HYPIC_BF16)
+        return fail(HYPIC_E_INVALID, "unknown input dtype %d", L->in_dtype);
+    if (L->n_chains < 1) return fail(HYPIC_E_INVALID, "n_chains must be >= 1 (got %d)", L->n_chains);
+    if (L->dk != 16 && L->dk != 32 && L->dk != 64 && L->dk != 128)
+        return fail(HYPIC_E_INVALID, "dk must be 16, 32, 64 or 128 (got %d)", L->dk);
+    if (L->dv != L->dk) return fail(HYPIC_E_UNSUPPORTED, "dv != dk is not supported (dk=%d dv=%d)", L->dk, L->dv);
+    return HYPIC_OK;
+}
+
+bool needs_g(int f) { return f == HYPIC_MAMBA2 || f == HYPIC_GDN || f == HYPIC_GLA || f == HYPIC_KDA; }
+bool needs_beta(int f) { return f == HYPIC_DELTANET || f == HYPIC_GDN || f == HYPIC_KDA; }
+bool vec_gate(int f) { return f == HYPIC_GLA || f == HYPIC_KDA; }
+
+// need_q: the op reads q (seam outputs).
+int check_tokens(const hypic_layout *L, const hypic_tokens *x, bool need_q) {
+    if (!x) return fail(HYPIC_E_INVALID, "token tensors are NULL");
+    const int es = esize(L->in_dtype);
+    if (!x->k || !x->v) return fail(HYPIC_E_INVALID, "k and v are required");
+    if (need_q && !x->q) return fail(HYPIC_E_INVALID, "q is required for seam outputs");
+    if (needs_g(L->family) && !x->g) return fail(HYPIC_E_INVALID, "this family needs log-gates g");
+    if (needs_beta(L->family) && !x->beta) return fail(HYPIC_E_INVALID, "this family needs beta");
+    if (L->family == HYPIC_RETNET && !x->gamma) return fail(HYPIC_E_INVALID, "RetNet needs gamma");
+    if (x->chain_stride < L->dk) return fail(HYPIC_E_INVALID, "chain_stride %lld < dk", (long long)x->chain_stride);
+    if (x->tok_stride < (int64_t)L->dk) return fail(HYPIC_E_INVALID, "tok_stride %lld < dk", (long long)x->tok_stride);
+    if (((x->tok_stride * es) & 15) || ((x->chain_stride * es) & 15))
+        return fail(HYPIC_E_INVALID, "q/k/v strides must be multiples of 16 bytes");
+    if (!aligned16(x->k) || !aligned16(x->v) || (need_q && !aligned16(x->q)))
+        return fail(HYPIC_E_INVALID, "q/k/v must be 16-byte aligned");
+    if (needs_g(L->family)) {
+        if (x->g_tok_stride < 0 || x->g_chain_stride < 0) return fail(HYPIC_E_INVALID, "negative g stride");
+        if (vec_gate(L->family) && (x->g_chain_stride < L->dk && L->n_chains > 1))
+            return fail(HYPIC_E_INVALID, "g_chain_stride < dk for a per-channel gate");
+    }
+    if (needs_beta(L->family) && (x->b_tok_stride < 0 || x->b_chain_stride < 0))
+        return fail(HYPIC_E_INVALID, "negative beta stride");
+    return HYPIC_OK;
+}
+
+hy::Tok to_tok(const hypic_tokens *x) {
+    hy::Tok t;
+    t.q = x->q;
+    t.k = x->k;
+    t.v = x->v;
+    t.g = x->g;
+    t.beta = x->beta;
+    t.gamma = x->gamma;
+    t.ts = x->tok_stride;
+    t.cs = x->chain_stride;
+    t.gts = x->g_tok_stride;
+    t.gcs = x->g_chain_stride;
+    t.bts = x->b_tok_stride;
+    t.bcs = x->b_chain_stride;
+    return t;
+}
+
+int launched(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(HYPIC_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool dense(int f) { return f == HYPIC_DELTANET || f == HYPIC_GDN || f == HYPIC_KDA; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t hypic_t_elems(int32_t family, int32_t dk) {
+    switch (family) {
+    case HYPIC_LINEAR:
+    case HYPIC_RETNET:
+    case HYPIC_MAMBA2: return 1;
+    case HYPIC_GLA: return dk;
+    case HYPIC_DELTANET:
+    case HYPIC_GDN:
+    case HYPIC_KDA: return (int64_t)dk * dk;
+    }
+    return 0;
+}
+
+size_t hypic_workspace_bytes(const hypic_layout *L, int32_t op, int32_t n_items, int64_t max_len) {
+    (void)L;
+    (void)n_items;
+    (void)max_len;
+    if (op == HYPIC_OP_COMPOSE_TREE) return 0;  // the tree scan is not built yet
+    return 0;
+}
+
+int hypic_segment_build(const hypic_layout *L, const hypic_tokens *x, int32_t n_seg, const int64_t *d_seg_begin,
+                        const int64_t *d_seg_end, int64_t max_seg_len, float *d_T, float *d_S, void *d_ws,
+                        size_t ws_bytes, void *stream) {
+    (void)d_ws;
+    (void)ws_bytes;
+    int rc = check_layout(L);
+    if (rc) return rc;
+    if ((rc = check_tokens(L, x, false))) return rc;
+    if (n_seg < 0) return fail(HYPIC_E_INVALID, "n_seg < 0");
+    if (max_seg_len < 0) return fail(HYPIC_E_INVALID, "max_seg_len < 0");
+    if (n_seg == 0) return ok();
+    if (!d_seg_begin || !d_seg_end || !d_T || !d_S) return fail(HYPIC_E_INVALID, "NULL segment or output pointer");
+    if ((int64_t)n_seg * L->n_chains > 0x7fffffff) return fail(HYPIC_E_INVALID, "n_seg * n_chains too large");
+    if (L->family == HYPIC_KDA) return fail(HYPIC_E_UNSUPPORTED, "KDA pair build is not available in this build");
+    hy::BuildArgs a;
+    a.x = to_tok(x);
+    a.n_chains = L->n_chains;
+    a.dk = L->dk;
+    a.seg_begin = d_seg_begin;
+    a.seg_end = d_seg_end;
+    a.T = d_T;
+    a.S = d_S;
+    const int D = padded_d(L->dk);
+    const bool bf = L->in_dtype == HYPIC_BF16;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (dense(L->family)) {
+        return launched(hy::build_dense(a, L->family, bf, D, n_seg, st), "dense build launch");
+    }
+    return launched(hy::build_diag(a, L->family, bf, D, n_seg, st), "diagonal build launch");
+}
+
+int hypic_compose(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t max_list_len, const int32_t *d_list_off,
+                  const int32_t *d_pair_id, int64_t n_slots, const float *d_T, const float *d_S,
+                  const hypic_tokens *seam, const int64_t *d_seam_begin, int32_t w, float *d_state, float *d_o,
+                  void *d_ws, size_t ws_bytes, void *stream) {
+    (void)d_ws;
+    (void)ws_bytes;
+    int rc = check_layout(L);
+    if (rc) return rc;
+    if (mode != HYPIC_SEQ && mode != HYPIC_TREE) return fail(HYPIC_E_INVALID, "unknown mode %d", mode);
+    if (n_req < 0 || max_list_len < 0 || n_slots < 0) return fail(HYPIC_E_INVALID, "negative size");
+    if (w < 0) return fail(HYPIC_E_INVALID, "w < 0");
+    if (n_req == 0) return ok();
+    if (!d_list_off || !d_state) return fail(HYPIC_E_INVALID, "NULL list or state pointer");
+    if (max_list_len > 0 && (!d_pair_id || !d_T || !d_S)) return fail(HYPIC_E_INVALID, "NULL pair pointer");
+    if ((int64_t)n_req * L->n_chains > 0x7fffffff) return fail(HYPIC_E_INVALID, "n_req * n_chains too large");
+    const bool has_seam = seam != nullptr && w > 0;
+    if (has_seam) {
+        if ((rc = check_tokens(L, seam, true))) return rc;
+        if (!d_seam_begin || !d_o) return fail(HYPIC_E_INVALID, "seams need d_seam_begin and d_o");
+    }
+    if (mode == HYPIC_TREE) return fail(HYPIC_E_UNSUPPORTED, "tree-mode compose is not available in this build");
+    hy::ComposeArgs a;
+    a.x = has_seam ? to_tok(seam) : hy::Tok{};
+    a.n_chains = L->n_chains;
+    a.dk = L->dk;
+    a.w = has_seam ? w : 0;
+    a.has_seam = has_seam ? 1 : 0;
+    a.list_off = d_list_off;
+    a.pair_id = d_pair_id;
+    a.T = d_T;
+    a.S = d_S;
+    a.t_elems = hypic_t_elems(L->family, L->dk);
+    a.seam_begin = d_seam_begin;
+    a.state = d_state;
+    a.o = d_o;
+    return launched(hy::compose_seq(a, L->family, L->in_dtype == HYPIC_BF16, padded_d(L->dk), n_req,
+                                    reinterpret_cast<hipStream_t>(stream)),
+                    "compose launch");
+}
+
+int hypic_seam_advance(const hypic_layout *L, const hypic_tokens *x, int32_t n_items, const int64_t *d_tok_begin,
+                       int32_t w, float *d_state, float *d_o, void *stream) {
+    int rc = check_layout(L);
+    if (rc) return rc;
+    if ((rc = check_tokens(L, x, true))) return rc;
+    if (n_items < 0) return fail(HYPIC_E_INVALID, "n_items < 0");
+    if (w < 0) return fail(HYPIC_E_INVALID, "w < 0");
+    if (n_items == 0 || w == 0) return ok();
+    if (!d_tok_begin || !d_state || !d_o) return fail(HYPIC_E_INVALID, "NULL pointer");
+    if ((int64_t)n_items * L->n_chains > 0x7fffffff) return fail(HYPIC_E_INVALID, "n_items * n_chains too large");
+    hy::SeamArgs a;
+    a.x = to_tok(x);
+    a.n_chains = L->n_chains;
+    a.dk = L->dk;
+    a.w = w;
+    a.tok_begin = d_tok_begin;
+    a.state = d_state;
+    a.o = d_o;
+    return launched(hy::seam_advance(a, L->family, L->in_dtype == HYPIC_BF16, padded_d(L->dk), n_items,
+                                     reinterpret_cast<hipStream_t>(stream)),
+                    "seam advance launch");
+}
+
+const char *hypic_status_string(int status) {
+    switch (status) {
+    case HYPIC_OK: return "ok";
+    case HYPIC_E_INVALID: return "invalid argument";
+    case HYPIC_E_UNSUPPORTED: return "unsupported";
+    case HYPIC_E_WORKSPACE: return "workspace too small";
+    case HYPIC_E_DEVICE: return "device error";
+    }
+    return "unknown status";
+}
+
+const char *hypic_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,162 @@
+// Internal helpers shared by the libhypic kernels (gfx950 / CDNA4 only).
+//
+// Matrix-core convention used throughout: v_mfma_f32_16x16x32_bf16 computes a
+// 16x16 fp32 tile D += A(16x32) B(32x16).  Lane l (r16 = l % 16, grp = l / 16)
+// holds 8 bf16 of A's row r16 and 8 bf16 of B's column r16, and after the op
+// holds D[4*grp + jj][r16] for jj = 0..3 (the "C layout").  The hardware pairs
+// A element e with B element e of the same lane group, so the eight k values a
+// lane group covers may be any fixed subset of the 32 as long as A and B use
+// the same one.  Two subsets are used:
+//   contiguous: k = 8*grp + e                 (both operands read from LDS)
+//   permuted:   k = 4*grp + e        (e < 4)
+//               k = 16 + 4*grp + e-4 (e >= 4) (one operand is a C-layout
+//               accumulator pair: rows 4*grp+jj of two stacked 16-row tiles)
+// The permuted subset lets a state kept in accumulators feed the next product
+// directly, without a round trip through LDS.
+//
+// fp32 accuracy on bf16 matrix cores: x = hi + lo with hi = bf16(x) and
+// lo = bf16(x - hi) (the residual is exact in fp32).  x*y is taken as
+// hi*hi + hi*lo + lo*hi (three passes, relative error ~2^-17) or, when one
+// operand is exactly a bf16 value, as two passes.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hy {
+
+constexpr int CH = 64;  // tokens per chunk of the chunked (UT/WY) build
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+enum Family { LINEAR = 0, RETNET = 1, MAMBA2 = 2, GLA = 3, DELTANET = 4, GDN = 5, KDA = 6 };
+
+__host__ __device__ constexpr bool fam_dense(int f) { return f == DELTANET || f == GDN || f == KDA; }
+__host__ __device__ constexpr bool fam_beta(int f) { return f == DELTANET || f == GDN || f == KDA; }
+__host__ __device__ constexpr bool fam_vgate(int f) { return f == GLA || f == KDA; }
+__host__ __device__ constexpr bool fam_sgate(int f) { return f == MAMBA2 || f == GDN; }
+
+// Token tensors, strides in elements (innermost feature axis contiguous).
+struct Tok {
+    const void *q, *k, *v, *g, *beta;
+    const float *gamma;
+    int64_t ts, cs;    // q, k, v: token, chain
+    int64_t gts, gcs;  // g
+    int64_t bts, bcs;  // beta
+};
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ void split1(float x, bf16 &h, bf16 &l) {
+    h = (bf16)x;
+    l = (bf16)(x - (float)h);
+}
+
+// Split eight fp32 values into hi / lo bf16 vectors.
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &h, bf16x8 &l) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        bf16 hh = (bf16)x[e];
+        h[e] = hh;
+        l[e] = (bf16)(x[e] - (float)hh);
+    }
+}
+
+// 8 bf16 of row `row` of a row-major LDS matrix, permuted k subset at kbase.
+__device__ __forceinline__ bf16x8 lds_perm(const bf16 *M, int ld, int row, int kbase, int grp) {
+    const bf16 *p = M + row * ld + kbase + 4 * grp;
+    bf16x4 a = *reinterpret_cast<const bf16x4 *>(p);
+    bf16x4 b = *reinterpret_cast<const bf16x4 *>(p + 16);
+    bf16x8 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+    r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+    return r;
+}
+
+// 8 bf16 of row `row`, contiguous k subset at kbase.
+__device__ __forceinline__ bf16x8 lds_cont(const bf16 *M, int ld, int row, int kbase, int grp) {
+    return *reinterpret_cast<const bf16x8 *>(M + row * ld + kbase + 8 * grp);
+}
+
+// Gather the permuted-k B operand of one 32-row k block from two stacked
+// C-layout accumulator tiles (rows 0..15 in `top`, rows 16..31 in `bot`).
+__device__ __forceinline__ void acc_to_perm(const f32x4 &top, const f32x4 &bot, float (&x)[8]) {
+    x[0] = top[0]; x[1] = top[1]; x[2] = top[2]; x[3] = top[3];
+    x[4] = bot[0]; x[5] = bot[1]; x[6] = bot[2]; x[7] = bot[3];
+}
+
+template <typename T>
+__device__ __forceinline__ float ldf(const T *p) { return (float)(*p); }
+
+// Load 8 consecutive elements as fp32 (16-byte aligned for bf16, 32 for fp32).
+__device__ __forceinline__ void load8(const bf16 *p, float (&x)[8]) {
+    bf16x8 v = *reinterpret_cast<const bf16x8 *>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+}
+__device__ __forceinline__ void load8(const float *p, float (&x)[8]) {
+    f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+    f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+    x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+    x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
+}
+
+__device__ __forceinline__ float wave_sum16x(float v) {
+    // sum over the four lane groups that share r16 (lanes l, l^16, l^32, l^48)
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+}  // namespace hy
+
+namespace hy {
+
+// ---- fp32 matrix-core path (fp32 inputs): the same 8-element k subsets, each
+// element position e taken by one v_mfma_f32_16x16x4_f32 (k = lane group).
+__device__ __forceinline__ void lds_cont_f(const float *M, int ld, int row, int kbase, int grp, float (&x)[8]) {
+    const float *p = M + row * ld + kbase + 8 * grp;
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+    x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+    x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
+}
+
+__device__ __forceinline__ void lds_perm_f(const float *M, int ld, int row, int kbase, int grp, float (&x)[8]) {
+    const float *p = M + row * ld + kbase + 4 * grp;
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 16);
+    x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+    x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
+}
+
+__device__ __forceinline__ f32x4 mma_f32(const float (&a)[8], const float (&b)[8], f32x4 c) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
+    return c;
+}
+
+// D += A B with fp32 fragments: fp32 matrix cores (F32) or the three-pass
+// bf16 split (hi*hi + hi*lo + lo*hi).
+template <bool F32>
+__device__ __forceinline__ f32x4 mma_split(const float (&a)[8], const float (&b)[8], f32x4 c) {
+    if constexpr (F32) {
+        return mma_f32(a, b, c);
+    } else {
+        bf16x8 ah, al, bh, bl;
+        split8(a, ah, al);
+        split8(b, bh, bl);
+        c = mfma(ah, bh, c);
+        c = mfma(ah, bl, c);
+        c = mfma(al, bh, c);
+        return c;
+    }
+}
+
+}  // namespace hy

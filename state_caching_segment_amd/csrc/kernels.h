@@ -1,0 +1,52 @@
+// Launchers of the libhypic kernels (internal; the C ABI is in include/hypic.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace hy {
+
+struct BuildArgs {
+    Tok x;
+    int n_chains;
+    int dk;
+    const int64_t *seg_begin;
+    const int64_t *seg_end;
+    float *T;  // [seg][chain][t_elems]
+    float *S;  // [seg][chain][dk][dk]
+};
+
+struct ComposeArgs {
+    Tok x;  // seam tokens (q, k, v, g, beta, gamma)
+    int n_chains;
+    int dk;
+    int w;
+    int has_seam;
+    const int32_t *list_off;
+    const int32_t *pair_id;
+    const float *T;
+    const float *S;
+    int64_t t_elems;
+    const int64_t *seam_begin;
+    float *state;  // [req][chain][dk][dk]
+    float *o;      // [entry][w][chain][dk]
+};
+
+struct SeamArgs {
+    Tok x;
+    int n_chains;
+    int dk;
+    int w;
+    const int64_t *tok_begin;
+    float *state;  // [item][chain][dk][dk]
+    float *o;      // [item][w][chain][dk]
+};
+
+// D is the padded state size (32, 64 or 128) the kernel is instantiated for.
+hipError_t build_dense(const BuildArgs &a, int family, bool bf16_in, int D, int n_seg, hipStream_t st);
+hipError_t build_diag(const BuildArgs &a, int family, bool bf16_in, int D, int n_seg, hipStream_t st);
+hipError_t compose_seq(const ComposeArgs &a, int family, bool bf16_in, int D, int n_req, hipStream_t st);
+hipError_t seam_advance(const SeamArgs &a, int family, bool bf16_in, int D, int n_items, hipStream_t st);
+
+}  // namespace hy

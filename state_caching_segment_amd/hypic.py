@@ -1,0 +1,153 @@
+"""Python binding of libhypic (argument marshalling only).
+
+Each function has the name and argument order of its C counterpart in
+``include/hypic.h``; tensors are torch tensors whose data pointers are passed
+through, and a negative status raises ``HypicError`` with the library's own
+message.  All compute runs in the HIP kernels of ``libhypic.so``; nothing
+here falls back to another implementation: without the built library every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhypic.so")
+
+FAMILY = {"linear": 0, "retnet": 1, "mamba2": 2, "gla": 3, "deltanet": 4, "gdn": 5, "kda": 6}
+DTYPE = {"f32": 0, "bf16": 1}
+SEQ, TREE = 0, 1
+OP_BUILD, OP_COMPOSE_SEQ, OP_COMPOSE_TREE, OP_SEAM = 0, 1, 2, 3
+STATUS = {0: "HYPIC_OK", -1: "HYPIC_E_INVALID", -2: "HYPIC_E_UNSUPPORTED", -3: "HYPIC_E_WORKSPACE",
+          -4: "HYPIC_E_DEVICE"}
+EXPORTS = ("hypic_t_elems", "hypic_workspace_bytes", "hypic_segment_build", "hypic_compose",
+           "hypic_seam_advance", "hypic_status_string", "hypic_last_error")
+
+
+class HypicError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class hypic_layout(ctypes.Structure):
+    _fields_ = [("family", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("n_chains", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32)]
+
+
+class hypic_tokens(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("g", ctypes.c_void_p),
+                ("beta", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("tok_stride", ctypes.c_int64), ("chain_stride", ctypes.c_int64),
+                ("g_tok_stride", ctypes.c_int64), ("g_chain_stride", ctypes.c_int64),
+                ("b_tok_stride", ctypes.c_int64), ("b_chain_stride", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libhypic.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libhypic is not built ({path} missing); run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.hypic_t_elems.argtypes = [i32, i32]
+    lib.hypic_t_elems.restype = i64
+    lib.hypic_workspace_bytes.argtypes = [P, i32, i32, i64]
+    lib.hypic_workspace_bytes.restype = sz
+    lib.hypic_segment_build.argtypes = [P, P, i32, P, P, i64, P, P, P, sz, P]
+    lib.hypic_segment_build.restype = ctypes.c_int
+    lib.hypic_compose.argtypes = [P, i32, i32, i32, P, P, i64, P, P, P, P, i32, P, P, P, sz, P]
+    lib.hypic_compose.restype = ctypes.c_int
+    lib.hypic_seam_advance.argtypes = [P, P, i32, P, i32, P, P, P]
+    lib.hypic_seam_advance.restype = ctypes.c_int
+    lib.hypic_status_string.argtypes = [ctypes.c_int]
+    lib.hypic_status_string.restype = ctypes.c_char_p
+    lib.hypic_last_error.argtypes = []
+    lib.hypic_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _p(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise HypicError(rc, load().hypic_last_error().decode())
+
+
+def layout(family: str, in_dtype: str, n_chains: int, dk: int, dv: Optional[int] = None) -> hypic_layout:
+    return hypic_layout(FAMILY[family], DTYPE[in_dtype], n_chains, dk, dk if dv is None else dv)
+
+
+def tokens(q=None, k=None, v=None, g=None, beta=None, gamma=None) -> hypic_tokens:
+    """hypic_tokens from token-major tensors x[token][chain][feature] (any strides
+    whose feature axis is contiguous); g is [token][chain] or [token][chain][dk],
+    beta [token][chain], gamma [chain] fp32."""
+    ref = k if k is not None else q
+    tok = hypic_tokens()
+    tok.q, tok.k, tok.v = _p(q), _p(k), _p(v)
+    tok.g, tok.beta, tok.gamma = _p(g), _p(beta), _p(gamma)
+    if ref is not None:
+        tok.tok_stride, tok.chain_stride = ref.stride(0), ref.stride(1)
+    if g is not None:
+        tok.g_tok_stride, tok.g_chain_stride = g.stride(0), g.stride(1)
+    if beta is not None:
+        tok.b_tok_stride, tok.b_chain_stride = beta.stride(0), beta.stride(1)
+    return tok
+
+
+def hypic_t_elems(family: str, dk: int) -> int:
+    return int(load().hypic_t_elems(FAMILY[family], dk))
+
+
+def hypic_workspace_bytes(L: hypic_layout, op: int, n_items: int, max_len: int) -> int:
+    return int(load().hypic_workspace_bytes(ctypes.byref(L), op, n_items, max_len))
+
+
+def hypic_segment_build(L: hypic_layout, x: hypic_tokens, n_seg: int, seg_begin, seg_end, max_seg_len: int,
+                        T, S, ws=None, ws_bytes: int = 0, stream=None) -> None:
+    _check(load().hypic_segment_build(ctypes.byref(L), ctypes.byref(x), n_seg, _p(seg_begin), _p(seg_end),
+                                      int(max_seg_len), _p(T), _p(S), _p(ws), ws_bytes, _stream(stream)))
+
+
+def hypic_compose(L: hypic_layout, mode: int, n_req: int, max_list_len: int, list_off, pair_id, n_slots: int,
+                  T, S, seam: Optional[hypic_tokens], seam_begin, w: int, state, o, ws=None, ws_bytes: int = 0,
+                  stream=None) -> None:
+    _check(load().hypic_compose(ctypes.byref(L), mode, n_req, max_list_len, _p(list_off), _p(pair_id), n_slots,
+                                _p(T), _p(S), ctypes.byref(seam) if seam is not None else None, _p(seam_begin), w,
+                                _p(state), _p(o), _p(ws), ws_bytes, _stream(stream)))
+
+
+def hypic_seam_advance(L: hypic_layout, x: hypic_tokens, n_items: int, tok_begin, w: int, state, o,
+                       stream=None) -> None:
+    _check(load().hypic_seam_advance(ctypes.byref(L), ctypes.byref(x), n_items, _p(tok_begin), w, _p(state), _p(o),
+                                     _stream(stream)))
+
+
+def hypic_status_string(status: int) -> str:
+    return load().hypic_status_string(status).decode()
+
+
+def hypic_last_error() -> str:
+    return load().hypic_last_error().decode()

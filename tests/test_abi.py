@@ -1,0 +1,127 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/hypic.h declares, and rejects bad arguments with the documented
+status before making any HIP call.  Also the host-side request plan."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import state_caching_segment_amd as hy
+from state_caching_segment_amd.plan import request_plan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hypic.h")
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hypic_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = hy.load()
+    names = declared()
+    assert set(names) == set(hy.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_t_elems_and_status_strings():
+    assert hy.hypic_t_elems("retnet", 64) == 1
+    assert hy.hypic_t_elems("gla", 64) == 64
+    assert hy.hypic_t_elems("kda", 128) == 128 * 128
+    assert hy.hypic_status_string(0) == "ok"
+    assert hy.hypic_status_string(-2) == "unsupported"
+    assert hy.load().hypic_t_elems(99, 16) == 0
+
+
+def _fake_tokens(family, dtype="bf16", align=0, ts=None, cs=128):
+    base = 1 << 20  # never dereferenced: validation fails or returns before any HIP call
+    t = hy.hypic_tokens()
+    t.q = t.k = t.v = base + align
+    t.g = base if family in ("mamba2", "gdn", "gla", "kda") else None
+    t.beta = base if family in ("deltanet", "gdn", "kda") else None
+    t.gamma = base if family == "retnet" else None
+    t.tok_stride = ts if ts is not None else 4 * cs
+    t.chain_stride = cs
+    t.g_tok_stride, t.g_chain_stride = 4 * 128, 128
+    t.b_tok_stride, t.b_chain_stride = 4, 1
+    return t
+
+
+def expect(status, fn, *args):
+    with pytest.raises(hy.HypicError) as e:
+        fn(*args)
+    assert e.value.status == status, str(e.value)
+    assert hy.hypic_last_error() != ""
+
+
+def test_build_validation():
+    L = hy.layout("gdn", "bf16", 4, 128)
+    x = _fake_tokens("gdn")
+    b = hy.hypic_segment_build
+    expect(-1, b, hy.layout("gdn", "bf16", 4, 100), x, 1, 8, 8, 10, 8, 8)       # bad dk
+    expect(-2, b, hy.layout("gdn", "bf16", 4, 128, 64), x, 1, 8, 8, 10, 8, 8)   # dv != dk
+    expect(-1, b, hy.layout("gdn", "bf16", 0, 128), x, 1, 8, 8, 10, 8, 8)      # no chains
+    bad = hy.hypic_layout(9, 1, 4, 128, 128)
+    expect(-1, b, bad, x, 1, 8, 8, 10, 8, 8)                                    # family
+    bad = hy.hypic_layout(5, 7, 4, 128, 128)
+    expect(-1, b, bad, x, 1, 8, 8, 10, 8, 8)                                    # dtype
+    expect(-1, b, L, _fake_tokens("gdn", align=2), 1, 8, 8, 10, 8, 8)          # misaligned k
+    expect(-1, b, L, _fake_tokens("gdn", ts=4 * 128 + 1), 1, 8, 8, 10, 8, 8)   # stride not 16 B
+    expect(-1, b, L, _fake_tokens("gdn", cs=64), 1, 8, 8, 10, 8, 8)           # chain stride < dk
+    x2 = _fake_tokens("gdn")
+    x2.g = None
+    expect(-1, b, L, x2, 1, 8, 8, 10, 8, 8)                                    # missing gate
+    x3 = _fake_tokens("gdn")
+    x3.beta = None
+    expect(-1, b, L, x3, 1, 8, 8, 10, 8, 8)                                    # missing beta
+    expect(-1, b, hy.layout("retnet", "f32", 4, 128), _fake_tokens("linear", "f32"), 1, 8, 8, 10, 8, 8)  # gamma
+    expect(-1, b, L, x, -1, 8, 8, 10, 8, 8)                                    # n_seg < 0
+    expect(-1, b, L, x, 2, None, 8, 10, 8, 8)                                  # NULL begin
+    expect(-1, b, L, x, 2, 8, 8, 10, None, 8)                                  # NULL T
+    b(L, x, 0, None, None, 0, None, None)  # nothing to do: OK without touching the device
+
+
+def test_compose_and_seam_validation():
+    L = hy.layout("gdn", "bf16", 4, 64)
+    x = _fake_tokens("gdn", cs=64)
+    c = hy.hypic_compose
+    expect(-1, c, L, 5, 1, 2, 8, 8, 2, 8, 8, None, None, 0, 8, None)           # mode
+    expect(-1, c, L, hy.SEQ, 1, 2, 8, 8, 2, 8, 8, x, 8, -1, 8, 8)              # w < 0
+    expect(-1, c, L, hy.SEQ, 1, 2, None, 8, 2, 8, 8, None, None, 0, 8, None)   # NULL list
+    expect(-1, c, L, hy.SEQ, 1, 2, 8, 8, 2, 8, 8, x, None, 8, 8, 8)            # seams without begin
+    expect(-1, c, L, hy.SEQ, 1, 2, 8, 8, 2, 8, 8, x, 8, 8, 8, None)            # seams without outputs
+    xq = _fake_tokens("gdn", cs=64)
+    xq.q = None
+    expect(-1, c, L, hy.SEQ, 1, 2, 8, 8, 2, 8, 8, xq, 8, 8, 8, 8)              # seams need q
+    expect(-2, c, L, hy.TREE, 1, 2, 8, 8, 2, 8, 8, None, None, 0, 8, None)     # not built
+    c(L, hy.SEQ, 0, 0, None, None, 0, None, None, None, None, 0, None, None)   # empty: OK
+    s = hy.hypic_seam_advance
+    expect(-1, s, L, x, 2, None, 8, 8, 8)
+    expect(-1, s, L, x, 2, 8, -3, 8, 8)
+    s(L, x, 0, None, 8, None, None)
+
+
+def test_workspace_query():
+    L = hy.layout("gdn", "bf16", 4, 128)
+    assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_SEQ, 4, 48) == 0
+    assert hy.hypic_workspace_bytes(L, hy.OP_BUILD, 4, 48) == 0
+
+
+def test_request_plan():
+    reqs = [np.array([0, 100, 150, 300]), np.array([300, 420, 500])]
+    p = request_plan(reqs, 8)
+    assert p.n_slots == 5 and p.n_req == 2
+    assert p.seg_begin.tolist() == [0, 108, 158, 300, 428]
+    assert p.seg_end.tolist() == [100, 150, 300, 420, 500]
+    assert p.seam_begin.tolist() == [-1, 100, 150, -1, 420]
+    assert p.list_off.tolist() == [0, 3, 5]
+    assert p.max_seg_len == 142 and p.max_list_len == 3
+    p0 = request_plan(reqs, 0)
+    assert p0.seg_begin.tolist() == [0, 100, 150, 300, 420] and (p0.seam_begin == -1).all()
+    with pytest.raises(ValueError):
+        request_plan([np.array([0, 100, 108])], 8)
