@@ -1,0 +1,214 @@
+"""Benchmark of the linear-layer segment state caching hot path on one GPU.
+
+One step = the whole path over one synthetic request:
+  1. hypic_segment_build: the cached pair (T_C, S(C|0)) of every segment body
+     on every chain;
+  2. hypic_compose: the request's running state assembled from those pairs,
+     advancing through the w = 8 seam tokens of every internal segment and
+     emitting their outputs.
+Default workload: Gated DeltaNet, bf16 inputs with fp32 state, 30 layers x 32
+heads = 960 chains, d = 128, one 32768-token request in 48 segments
+(lognormal lengths, min 512, mean ~683), seams of 8 tokens on the 47 internal
+segments.  Inputs are seeded synthetic tensors generated on the GPU and
+resident in HBM before timing starts.
+
+Printed: one JSON line with build tokens/s (request tokens / build time) as
+`value`, the compose latency, each kernel's roofline fraction, and the fp64
+oracle timed on the host on a bounded sample of chains.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+import state_caching_segment_amd as hy  # noqa: E402
+from state_caching_segment_amd.plan import request_plan  # noqa: E402
+
+METRIC = "(T_C,S0) build tokens/s + 32k-request state-compose latency (ms), 1 GPU"
+HBM_PEAK = 8.0e12        # B/s, MI355X HBM3E
+BF16_PEAK = 2.5e15       # FLOP/s, dense bf16 MFMA
+FP32_MFMA_PEAK = 157.3e12
+CH = 64
+
+
+def build_cost(lens, d, n_chains, in_bytes):
+    """Algorithmic flops and HBM bytes of building the pairs of segments with
+    the given lengths (chunked UT/WY form, c = 64):
+      per chunk of c tokens: carry of [T|S] 8 c d^2 (4 c d^2 for a segment's
+      first chunk, which starts from [I|0]), Gram c(c-1)d, unit-lower inverse
+      c^3/3, W and U 2 c^2 d;
+      bytes: k, v (d each), g and beta (1 each) per token read once, and the
+      fp32 pair (T and S, d^2 each) written once."""
+    flops = 0.0
+    for n in lens:
+        for j, c0 in enumerate(range(0, int(n), CH)):
+            c = min(CH, int(n) - c0)
+            carry = 8 * c * d * d if j > 0 else 4 * c * d * d
+            flops += carry + c * (c - 1) * d + c ** 3 / 3 + 2 * c * c * d
+    tokens = float(np.sum(lens))
+    byts = tokens * (2 * d + 2) * in_bytes + len(lens) * 2 * d * d * 4
+    return flops * n_chains, byts * n_chains
+
+
+def compose_cost(n_entries, n_seams, w, d, n_chains, in_bytes):
+    """Algorithmic flops and bytes of one sequential compose with seams: every
+    pair read once (fp32 T and S), per seam token q, k, v (d each), g and beta
+    read and o (d, fp32) written, initial and final state; flops 2 d^3 per
+    pair after the first (T S) and ~7 d^2 per seam token."""
+    flops = (n_entries - 1) * 2 * d ** 3 + n_seams * w * 7 * d * d
+    byts = n_entries * 2 * d * d * 4 + n_seams * w * ((3 * d + 2) * in_bytes + d * 4) + 2 * d * d * 4
+    return flops * n_chains, byts * n_chains
+
+
+def cpu_baseline(wl, n_chains_sample, w):
+    """The fp64 oracle (build every pair token by token, compose, seams) on a
+    sample of chains, all host threads; scaled to request tokens/s for all
+    chains."""
+    import oracle
+    chains = list(range(n_chains_sample))
+    b = wl.requests[0]
+
+    def cm(x):
+        if x is None:
+            return None
+        return np.ascontiguousarray(np.moveaxis(x[:, chains].double().cpu().numpy(), 1, 0))
+
+    q, k, v, g, beta = cm(wl.q), cm(wl.k), cm(wl.v), cm(wl.g), cm(wl.beta)
+    gam = None if wl.gamma is None else wl.gamma[chains].double().cpu().numpy()
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.request_batch(wl.family, b - b[0], w, q, k, v, g, beta, gam, want_pairs=False, nthreads=threads)
+    dt = time.perf_counter() - t0
+    tok = float(b[-1] - b[0])
+    return {"value": tok * n_chains_sample / (wl.n_chains * dt), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n_chains_sample} of {wl.n_chains} chains, full {int(tok)}-token request "
+                      f"(all pairs + compose + seams), {dt:.1f} s; scaled by chains"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c4")
+    ap.add_argument("--cpu-chains", type=int, default=-1,
+                    help="chains in the oracle's CPU-baseline sample (-1: two per host thread; 0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path shards by chain with no "
+              f"exchange, so N GPUs would each run this same per-GPU workload).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    hy.load()
+
+    wl = workloads.config(args.config, device="cuda")
+    w = wl.w
+    plan = request_plan(wl.requests, w)
+    d, C = wl.dk, wl.n_chains
+    dev = "cuda"
+    L = hy.layout(wl.family, wl.dtype, C, d)
+    x = hy.tokens(wl.q, wl.k, wl.v, wl.g, wl.beta, wl.gamma)
+    te = hy.hypic_t_elems(wl.family, d)
+    T = torch.empty(plan.n_slots, C, te, device=dev)
+    S = torch.empty(plan.n_slots, C, d, d, device=dev)
+    sb = torch.from_numpy(plan.seg_begin).to(dev)
+    se = torch.from_numpy(plan.seg_end).to(dev)
+    lo = torch.from_numpy(plan.list_off).to(dev)
+    pid = torch.from_numpy(plan.pair_id).to(dev)
+    seam = torch.from_numpy(plan.seam_begin).to(dev)
+    state = torch.zeros(plan.n_req, C, d, d, device=dev)
+    o = torch.zeros(len(plan.pair_id), w, C, d, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        hy.hypic_segment_build(L, x, plan.n_slots, sb, se, plan.max_seg_len, T, S, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        state.zero_()
+        if ev:
+            ev[2].record(stream)
+        hy.hypic_compose(L, hy.SEQ, plan.n_req, plan.max_list_len, lo, pid, plan.n_slots, T, S, x, seam, w, state,
+                         o, stream=stream)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    b_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    c_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    step_ms = wall * 1e3 / args.steps
+
+    in_bytes = 2 if wl.dtype == "bf16" else 4
+    req_tokens = int(wl.requests[0][-1] - wl.requests[0][0])
+    bf, bb = build_cost(plan.seg_end - plan.seg_begin, d, C, in_bytes)
+    n_seams = int((plan.seam_begin >= 0).sum())
+    cf, cb = compose_cost(len(plan.pair_id), n_seams, w, d, C, in_bytes)
+    tb, tc = float(np.median(b_ms)) * 1e-3, float(np.median(c_ms)) * 1e-3
+    # the build's binding roof is the larger of its HBM and bf16-MFMA times
+    b_hbm, b_mfma = bb / tb, bf / tb
+    b_bound = "hbm" if bb / HBM_PEAK >= bf / BF16_PEAK else "mfma"
+    roof_build = ({"bound": "hbm", "achieved": b_hbm / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                   "frac": b_hbm / HBM_PEAK} if b_bound == "hbm" else
+                  {"bound": "mfma", "achieved": b_mfma / 1e12, "peak": BF16_PEAK / 1e12, "unit": "TFLOP/s",
+                   "frac": b_mfma / BF16_PEAK})
+    roof_build.update({"traffic": None, "kernel": "k_build_dense", "alg_bytes": bb, "alg_flops": bf,
+                       "mfma_frac_alg": b_mfma / BF16_PEAK, "hbm_frac_alg": b_hbm / HBM_PEAK})
+    roof_comp = {"bound": "hbm", "achieved": cb / tc / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                 "frac": cb / tc / HBM_PEAK, "traffic": None, "kernel": "k_compose_seq", "alg_bytes": cb,
+                 "alg_flops": cf}
+    out = {
+        "metric": METRIC,
+        "value": req_tokens / tb,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.family} pair build + seq compose with w={w} seams: {C} chains "
+                               f"(30 layers x 32 heads), d={d}, one {req_tokens}-token request, "
+                               f"{plan.n_slots} segments",
+                   "chains": C, "d": d, "request_tokens": req_tokens, "segments": plan.n_slots, "w": w,
+                   "state_dtype": "f32"},
+        "build_ms": float(np.median(b_ms)),
+        "build_ms_p10_p90": [float(np.percentile(b_ms, 10)), float(np.percentile(b_ms, 90))],
+        "compose_latency_ms": float(np.median(c_ms)),
+        "compose_ms_p10_p90": [float(np.percentile(c_ms, 10)), float(np.percentile(c_ms, 90))],
+        "chain_tokens_per_s_build": req_tokens * C / tb,
+        "roofline": roof_build,
+        "roofline_compose": roof_comp,
+    }
+    if args.cpu_chains != 0:
+        import oracle
+        n_cpu = 2 * oracle.max_threads() if args.cpu_chains < 0 else args.cpu_chains
+        out["cpu_baseline"] = cpu_baseline(wl, min(n_cpu, C), w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -140,6 +140,7 @@ int hypic_segment_build(const hypic_layout *L, const hypic_tokens *x, int32_t n_
     if (!d_seg_begin || !d_seg_end || !d_T || !d_S) return fail(HYPIC_E_INVALID, "NULL segment or output pointer");
     if ((int64_t)n_seg * L->n_chains > 0x7fffffff) return fail(HYPIC_E_INVALID, "n_seg * n_chains too large");
     if (L->family == HYPIC_KDA) return fail(HYPIC_E_UNSUPPORTED, "KDA pair build is not available in this build");
+    if (x->tok_stride > (1 << 24)) return fail(HYPIC_E_UNSUPPORTED, "tok_stride above 2^24 elements is not supported");
     hy::BuildArgs a;
     a.x = to_tok(x);
     a.n_chains = L->n_chains;

@@ -6,15 +6,22 @@
 // exp(g_t) (GDN) or 1 (DeltaNet), a chunk of c = 64 tokens is applied at once
 // in the UT / WY form (Gamma_t = chunk-local cumulative log-decay):
 //     G_ti = (k_t . k_i) exp(Gamma_t - Gamma_i)            for t > i
-//     A    = (I + diag(beta) tril(G, -1))^-1 diag(beta)     (unit lower solve)
-//     W    = A diag(exp(Gamma)) K,   U = A V
-//     X   <- exp(Gamma_c) X + K^T diag(exp(Gamma_c - Gamma)) ([0 | U] - W X)
-// on X = [T | S] (d x 2d), starting from [I | 0].
+//     Inv  = (I + diag(beta) tril(G, -1))^-1                (unit lower)
+//     X   <- exp(Gamma_c) X + K^T diag(exp(Gamma_c - Gamma)) R,
+//     R    = [0 | Inv diag(beta) V] - Inv diag(beta exp(Gamma)) (K X)
+// on X = [T | S] (d x 2d), starting from [I | 0].  (R is A([0|V] - K_L X)
+// with A = Inv diag(beta) and K_L = diag(exp Gamma) K: the UT transform's W
+// and U never need to be formed.)
 //
 // Mapping: one workgroup per (segment, chain), 2d/32 waves; wave w owns
 // columns 32w .. 32w+31 of X for the whole segment and keeps them in MFMA
-// accumulators (the columns of X evolve independently given the chunk's W,
-// U and K).  Chunk factors (Gram, inverse, W, U) are shared through LDS.
+// accumulators; every product of the carry takes the wave's own columns
+// straight from (and back to) its accumulators.  Per chunk the workgroup
+// stages K, K^T and V^T in LDS (loaded one chunk ahead into registers),
+// forms the Gram matrix on the matrix cores and inverts I + L in 16 x 16
+// blocks: diagonal blocks by forward substitution, off-diagonal blocks
+//     Inv_ij = -Inv_ii sum_{k=j}^{i-1} L_ik Inv_kj
+// by distance from the diagonal on the fp32 matrix cores.
 //
 // Precision: bf16 inputs use bf16 matrix cores; keys and values are exact in
 // bf16, every other operand is split into hi + lo (two or three passes, fp32
@@ -35,32 +42,51 @@ struct DenseCfg {
     static constexpr int NT = NW * 64;
     static constexpr int RT = D / 16;
     static constexpr int KB = D / 32;
+    static constexpr int ITEMS = CH * D / 8 / NT;      // 8-element rows of K (and V) per thread per chunk
     static constexpr int LDK = F32 ? D + 4 : D + 8;    // row stride of [CH][D] operand arrays
     static constexpr int LDT = F32 ? CH + 4 : CH + 8;  // row stride of [D][CH] operand arrays
     static constexpr int LDL = CH + 1;                 // fp32 row stride of L
-    static constexpr int LDI = CH + 4;                 // fp32 row stride of Inv and U^T
-    // region A: K rows (load, Gram), inverse scratch, then U^T (W/U, carry)
-    static constexpr int szK = CH * LDK * ES;
-    static constexpr int szP = 4 * 16 * 17 * 4;
-    static constexpr int szU = D * LDI * 4;
-    static constexpr int offA = 0;
-    static constexpr int szA = (((szK + szP) > szU ? (szK + szP) : szU) + 15) / 16 * 16;
-    static constexpr int offP = offA + szK;
-    // region B: L (Gram, inverse), then W (hi/lo bf16, or fp32) (W/U, carry)
-    static constexpr int szL = CH * LDL * 4;
-    static constexpr int szW = CH * LDK * 4;
-    static constexpr int offB = offA + szA;
-    static constexpr int szB = ((szL > szW ? szL : szW) + 15) / 16 * 16;
-    static constexpr int offKT = offB + szB;
-    static constexpr int szKT = D * LDT * ES;
-    static constexpr int offVT = offKT + szKT;
-    static constexpr int szVT = D * LDT * ES;
-    static constexpr int offInv = offVT + szVT;
-    static constexpr int szInv = CH * LDI * 4;
-    static constexpr int offSc = offInv + szInv;  // Gamma, exp(Gamma), exp(Gamma_c - Gamma), beta, lam
-    static constexpr int szSc = (4 * CH + 4) * 4;
-    static constexpr int total = offSc + szSc;
+    static constexpr int LDI = CH + 4;                 // fp32 row stride of Inv
+    static constexpr int al(int x) { return (x + 15) / 16 * 16; }
+    static constexpr int offK = 0;
+    static constexpr int offKT = offK + al(CH * LDK * ES);
+    static constexpr int offVT = offKT + al(D * LDT * ES);
+    // -Inv diag(beta exp Gamma) (Aw) and Inv diag(beta) (Au) as A operands: hi and lo
+    // bf16, or fp32.  Aw reuses L's space: L is dead once the inverse is formed.
+    static constexpr int LDA = F32 ? CH + 4 : CH + 8;
+    static constexpr int szA = F32 ? CH * LDA * 4 : 2 * CH * LDA * 2;
+    static constexpr int offL = offVT + al(D * LDT * ES);
+    static constexpr int offAw = offL;
+    static constexpr int offInv = offL + al(CH * LDL * 4 > szA ? CH * LDL * 4 : szA);
+    static constexpr int offAu = offInv + al(CH * LDI * 4);
+    static constexpr int offSc = offAu + al(szA);  // Gamma, beta, exp(Gc-Gamma), beta exp(Gamma), lam
+    static constexpr int total = offSc + (4 * CH + 4) * 4;
     static_assert(total <= 160 * 1024, "LDS budget");
+    static_assert(ITEMS * NT * 8 == CH * D, "staging split");
+};
+
+// Eight raw input elements held in registers between a prefetch and its use.
+template <typename TIN>
+struct Raw8;
+template <>
+struct Raw8<bf16> {
+    bf16x8 v;
+    __device__ void load(const bf16 *p) { v = *reinterpret_cast<const bf16x8 *>(p); }
+    __device__ void zero() {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (bf16)0.f;
+    }
+    __device__ float get(int e) const { return (float)v[e]; }
+};
+template <>
+struct Raw8<float> {
+    f32x4 a, b;
+    __device__ void load(const float *p) {
+        a = *reinterpret_cast<const f32x4 *>(p);
+        b = *reinterpret_cast<const f32x4 *>(p + 4);
+    }
+    __device__ void zero() { a = b = f32x4{0.f, 0.f, 0.f, 0.f}; }
+    __device__ float get(int e) const { return e < 4 ? a[e] : b[e - 4]; }
 };
 
 template <int D, int FAM, typename TIN>
@@ -69,24 +95,23 @@ k_build_dense(BuildArgs a) {
     using Cfg = DenseCfg<D, TIN>;
     constexpr bool F32 = Cfg::F32;
     using OpT = typename std::conditional<F32, float, bf16>::type;
-    constexpr int NW = Cfg::NW, NT = Cfg::NT, RT = Cfg::RT, KB = Cfg::KB;
-    constexpr int LDK = Cfg::LDK, LDT = Cfg::LDT, LDL = Cfg::LDL, LDI = Cfg::LDI;
+    constexpr int NW = Cfg::NW, NT = Cfg::NT, RT = Cfg::RT, KB = Cfg::KB, ITEMS = Cfg::ITEMS;
+    constexpr int LDK = Cfg::LDK, LDT = Cfg::LDT, LDL = Cfg::LDL, LDI = Cfg::LDI, LDA = Cfg::LDA;
     __shared__ __attribute__((aligned(16))) char smem[Cfg::total];
-    OpT *sK = reinterpret_cast<OpT *>(smem + Cfg::offA);
-    float *sP = reinterpret_cast<float *>(smem + Cfg::offP);
-    float *sU = reinterpret_cast<float *>(smem + Cfg::offA);
-    float *sL = reinterpret_cast<float *>(smem + Cfg::offB);
-    bf16 *sWh = reinterpret_cast<bf16 *>(smem + Cfg::offB);  // bf16 path: hi then lo
-    bf16 *sWl = sWh + CH * LDK;
-    float *sWf = reinterpret_cast<float *>(smem + Cfg::offB);  // fp32 path
+    OpT *sK = reinterpret_cast<OpT *>(smem + Cfg::offK);
     OpT *sKT = reinterpret_cast<OpT *>(smem + Cfg::offKT);
     OpT *sVT = reinterpret_cast<OpT *>(smem + Cfg::offVT);
+    float *sL = reinterpret_cast<float *>(smem + Cfg::offL);
     float *sInv = reinterpret_cast<float *>(smem + Cfg::offInv);
+    bf16 *sAwh = reinterpret_cast<bf16 *>(smem + Cfg::offAw), *sAwl = sAwh + CH * LDA;
+    bf16 *sAuh = reinterpret_cast<bf16 *>(smem + Cfg::offAu), *sAul = sAuh + CH * LDA;
+    float *sAwf = reinterpret_cast<float *>(smem + Cfg::offAw);
+    float *sAuf = reinterpret_cast<float *>(smem + Cfg::offAu);
     float *sGam = reinterpret_cast<float *>(smem + Cfg::offSc);
-    float *sEg = sGam + CH;
-    float *sEc = sEg + CH;
-    float *sBeta = sEc + CH;
-    float *sLam = sBeta + CH;
+    float *sBeta = sGam + CH;
+    float *sEc = sBeta + CH;
+    float *sAwS = sEc + CH;
+    float *sLam = sAwS + CH;
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
@@ -109,46 +134,78 @@ k_build_dense(BuildArgs a) {
             for (int jj = 0; jj < 4; ++jj)
                 X[rt][nt][jj] = (16 * rt + 4 * grp + jj == cbase + 16 * nt + r16) ? 1.f : 0.f;
 
-    for (int64_t c0 = 0; c0 < n; c0 += CH) {
+    // ---- inputs of the next chunk, prefetched into registers
+    Raw8<TIN> kpre[ITEMS], vpre[ITEMS];
+    TIN gpre = (TIN)0.f, bpre = (TIN)0.f;
+    // per-lane element offsets within a chunk (32-bit; the chunk base is wave-uniform)
+    int loff[ITEMS];
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+        // a wave covers 64 consecutive tokens of one 8-feature group, so the
+        // transposed LDS stores below are contiguous across lanes
+        const int item = tid + it * NT;
+        loff[it] = (item % CH) * (int)a.x.ts + (item / CH) * 8;
+    }
+    auto prefetch = [&](int64_t c0) {
         const int L = (int)(n - c0 < CH ? n - c0 : CH);
         const int64_t t0 = b0 + c0;
-        // ---- stage the chunk's keys and values (zero rows past the segment end)
-        for (int item = tid; item < CH * D / 8; item += NT) {
-            const int t = item / (D / 8), i8 = (item % (D / 8)) * 8;
-            float kv[8], vv[8];
+        const TIN *kc = kp + t0 * a.x.ts, *vc = vp + t0 * a.x.ts;
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+            const int item = tid + it * NT;
+            const int t = item % CH, i8 = (item / CH) * 8;
             if (t < L && i8 < dk) {
-                load8(kp + (t0 + t) * a.x.ts + i8, kv);
-                load8(vp + (t0 + t) * a.x.ts + i8, vv);
+                kpre[it].load(kc + loff[it]);
+                vpre[it].load(vc + loff[it]);
             } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) kv[e] = vv[e] = 0.f;
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                sK[t * LDK + i8 + e] = (OpT)kv[e];
-                sKT[(i8 + e) * LDT + t] = (OpT)kv[e];
-                sVT[(i8 + e) * LDT + t] = (OpT)vv[e];
+                kpre[it].zero();
+                vpre[it].zero();
             }
         }
         if (wv == 0) {
-            float gt = 0.f, bt = 0.f;
+            gpre = bpre = (TIN)0.f;
             if (lane < L) {
-                if (FAM == GDN) gt = ldf(gp + (t0 + lane) * a.x.gts);
-                bt = ldf(bp + (t0 + lane) * a.x.bts);
+                if (FAM == GDN) gpre = gp[(t0 + lane) * a.x.gts];
+                bpre = bp[(t0 + lane) * a.x.bts];
             }
-            float s = gt;
+        }
+    };
+    if (n > 0) prefetch(0);
+
+    for (int64_t c0 = 0; c0 < n; c0 += CH) {
+        // ---- stage the chunk (K rows, K^T, V^T) from registers; gate prefix sums
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+            const int item = tid + it * NT;
+            const int t = item % CH, i8 = (item / CH) * 8;
+            if constexpr (F32) {
+                *reinterpret_cast<f32x4 *>(sK + t * LDK + i8) = kpre[it].a;
+                *reinterpret_cast<f32x4 *>(sK + t * LDK + i8 + 4) = kpre[it].b;
+            } else {
+                *reinterpret_cast<bf16x8 *>(sK + t * LDK + i8) = kpre[it].v;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                sKT[(i8 + e) * LDT + t] = (OpT)kpre[it].get(e);
+                sVT[(i8 + e) * LDT + t] = (OpT)vpre[it].get(e);
+            }
+        }
+        if (wv == 0) {
+            float s = (float)gpre;
+            const float bt = (float)bpre;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
-                float y = __shfl_up(s, off);
+                const float y = __shfl_up(s, off);
                 if (lane >= off) s += y;
             }
             const float gc = __shfl(s, 63);
             sGam[lane] = s;
             sBeta[lane] = bt;
-            sEg[lane] = expf(s);
             sEc[lane] = expf(gc - s);
+            sAwS[lane] = bt * expf(s);
             if (lane == 0) sLam[0] = expf(gc);
         }
+        if (c0 + CH < n) prefetch(c0 + CH);
         __syncthreads();
 
         // ---- Gram of the chunk's keys, scaled into the strictly lower L
@@ -181,7 +238,7 @@ k_build_dense(BuildArgs a) {
         }
         __syncthreads();
 
-        // ---- (I + L)^-1 by 16 x 16 blocks: diagonal blocks by forward substitution
+        // ---- (I + L)^-1: diagonal 16 x 16 blocks by forward substitution
         if (wv == 0) {
             const int bk = grp, c = r16;
             float xr[16];
@@ -191,6 +248,7 @@ k_build_dense(BuildArgs a) {
 #pragma unroll
                 for (int j = 0; j < r; ++j) s -= sL[(16 * bk + r) * LDL + 16 * bk + j] * xr[j];
                 xr[r] = s;
+                __builtin_amdgcn_sched_barrier(0);  // keep each row's L loads next to their use
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) sInv[(16 * bk + r) * LDI + 16 * bk + c] = xr[r];
@@ -204,77 +262,49 @@ k_build_dense(BuildArgs a) {
             }
         }
         __syncthreads();
-        // off-diagonal blocks, by distance from the diagonal:
-        //   Inv_ij = -Inv_ii * sum_{k=j}^{i-1} L_ik Inv_kj
+        // off-diagonal blocks by distance d: P = sum_k L_ik Inv_kj, Inv_ij = -Inv_ii P,
+        // each 16 x 16 x 16 product as four v_mfma_f32_16x16x4_f32 (k = 4*grp + s)
         for (int d = 1; d < 4; ++d) {
             for (int blk = wv; blk < 4 - d; blk += NW) {
                 const int bi = blk + d, bj = blk;
-                float *sp = sP + blk * 16 * 17;
+                f32x4 P = {0.f, 0.f, 0.f, 0.f};
+                for (int kb = bj; kb < bi; ++kb) {
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int r = 4 * grp + jj;
-                    float acc = 0.f;
-                    for (int kb = bj; kb < bi; ++kb)
-#pragma unroll
-                        for (int m = 0; m < 16; ++m)
-                            acc += sL[(16 * bi + r) * LDL + 16 * kb + m] * sInv[(16 * kb + m) * LDI + 16 * bj + r16];
-                    sp[r * 17 + r16] = acc;
+                    for (int s = 0; s < 4; ++s)
+                        P = __builtin_amdgcn_mfma_f32_16x16x4f32(sL[(16 * bi + r16) * LDL + 16 * kb + 4 * grp + s],
+                                                                 sInv[(16 * kb + 4 * grp + s) * LDI + 16 * bj + r16],
+                                                                 P, 0, 0, 0);
                 }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                f32x4 O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int r = 4 * grp + jj;
-                    float acc = 0.f;
+                for (int s = 0; s < 4; ++s)
+                    O = __builtin_amdgcn_mfma_f32_16x16x4f32(sInv[(16 * bi + r16) * LDI + 16 * bi + 4 * grp + s], P[s],
+                                                             O, 0, 0, 0);
 #pragma unroll
-                    for (int m = 0; m < 16; ++m) acc += sInv[(16 * bi + r) * LDI + 16 * bi + m] * sp[m * 17 + r16];
-                    sInv[(16 * bi + r) * LDI + 16 * bj + r16] = -acc;
-                }
+                for (int jj = 0; jj < 4; ++jj) sInv[(16 * bi + 4 * grp + jj) * LDI + 16 * bj + r16] = -O[jj];
             }
             __syncthreads();
         }
-
-        // ---- W = A diag(exp Gamma) K and U = A V on the matrix cores
-        for (int tile = wv; tile < 8 * RT; tile += NW) {
-            const bool isU = tile >= 4 * RT;
-            const int rem = isU ? tile - 4 * RT : tile;
-            const int mt = rem / RT, nt = rem % RT;
-            const OpT *Bm = isU ? sVT : sKT;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        // A operands of the carry: Aw = -Inv diag(beta exp Gamma), Au = Inv diag(beta)
+        for (int idx = tid; idx < CH * CH / 4; idx += NT) {
+            const int t = idx / (CH / 4), i4 = (idx % (CH / 4)) * 4;
+            const f32x4 iv = *reinterpret_cast<const f32x4 *>(sInv + t * LDI + i4);
+            const f32x4 sw = *reinterpret_cast<const f32x4 *>(sAwS + i4);
+            const f32x4 su = *reinterpret_cast<const f32x4 *>(sBeta + i4);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const int i0 = 32 * kb + 8 * grp;
-                const float *ip = sInv + (16 * mt + r16) * LDI + i0;
-                float av[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) av[e] = ip[e] * (isU ? sBeta[i0 + e] : sBeta[i0 + e] * sEg[i0 + e]);
+            for (int e = 0; e < 4; ++e) {
+                const float w = -iv[e] * sw[e], u = iv[e] * su[e];
                 if constexpr (F32) {
-                    float bv[8];
-                    lds_cont_f(Bm, LDT, 16 * nt + r16, 32 * kb, grp, bv);
-                    acc = mma_f32(av, bv, acc);
+                    sAwf[t * LDA + i4 + e] = w;
+                    sAuf[t * LDA + i4 + e] = u;
                 } else {
-                    bf16x8 ah, al;
-                    split8(av, ah, al);
-                    const bf16x8 bh = lds_cont(Bm, LDT, 16 * nt + r16, 32 * kb, grp);
-                    acc = mfma(ah, bh, acc);
-                    acc = mfma(al, bh, acc);
-                }
-            }
-            if (isU) {
-                *reinterpret_cast<f32x4 *>(sU + (16 * nt + r16) * LDI + 16 * mt + 4 * grp) = acc;
-            } else {
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int t = 16 * mt + 4 * grp + jj, i = 16 * nt + r16;
-                    if constexpr (F32) {
-                        sWf[t * LDK + i] = acc[jj];
-                    } else {
-                        bf16 h, l;
-                        split1(acc[jj], h, l);
-                        sWh[t * LDK + i] = h;
-                        sWl[t * LDK + i] = l;
-                    }
+                    bf16 h, l;
+                    split1(w, h, l);
+                    sAwh[t * LDA + i4 + e] = h;
+                    sAwl[t * LDA + i4 + e] = l;
+                    split1(u, h, l);
+                    sAuh[t * LDA + i4 + e] = h;
+                    sAul[t * LDA + i4 + e] = l;
                 }
             }
         }
@@ -282,12 +312,12 @@ k_build_dense(BuildArgs a) {
 
         // ---- carry this wave's 32 columns of X = [T | S] through the chunk
         {
-            f32x4 M[4][2];
+            // Z = K X
+            f32x4 Z[4][2];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) M[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            // M = W X
+                for (int nt = 0; nt < 2; ++nt) Z[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 float xv[2][8];
@@ -296,10 +326,10 @@ k_build_dense(BuildArgs a) {
                 if constexpr (F32) {
 #pragma unroll
                     for (int mt = 0; mt < 4; ++mt) {
-                        float wf[8];
-                        lds_perm_f(sWf, LDK, 16 * mt + r16, 32 * kb, grp, wf);
+                        float kf[8];
+                        lds_perm_f(sK, LDK, 16 * mt + r16, 32 * kb, grp, kf);
 #pragma unroll
-                        for (int nt = 0; nt < 2; ++nt) M[mt][nt] = mma_f32(wf, xv[nt], M[mt][nt]);
+                        for (int nt = 0; nt < 2; ++nt) Z[mt][nt] = mma_f32(kf, xv[nt], Z[mt][nt]);
                     }
                 } else {
                     bf16x8 xh[2], xl[2];
@@ -307,45 +337,96 @@ k_build_dense(BuildArgs a) {
                     for (int nt = 0; nt < 2; ++nt) split8(xv[nt], xh[nt], xl[nt]);
 #pragma unroll
                     for (int mt = 0; mt < 4; ++mt) {
-                        const bf16x8 wh = lds_perm(sWh, LDK, 16 * mt + r16, 32 * kb, grp);
-                        const bf16x8 wl = lds_perm(sWl, LDK, 16 * mt + r16, 32 * kb, grp);
+                        const bf16x8 kh = lds_perm(sK, LDK, 16 * mt + r16, 32 * kb, grp);
 #pragma unroll
                         for (int nt = 0; nt < 2; ++nt) {
-                            M[mt][nt] = mfma(wh, xh[nt], M[mt][nt]);
-                            M[mt][nt] = mfma(wh, xl[nt], M[mt][nt]);
-                            M[mt][nt] = mfma(wl, xh[nt], M[mt][nt]);
+                            Z[mt][nt] = mfma(kh, xh[nt], Z[mt][nt]);
+                            Z[mt][nt] = mfma(kh, xl[nt], Z[mt][nt]);
                         }
                     }
                 }
             }
-            // R' = diag(exp(Gamma_c - Gamma)) ([0 | U] - M)
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const f32x4 ec = *reinterpret_cast<const f32x4 *>(sEc + 16 * mt + 4 * grp);
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    f32x4 u = {0.f, 0.f, 0.f, 0.f};
-                    if (isS) u = *reinterpret_cast<const f32x4 *>(sU + (cbase - D + 16 * nt + r16) * LDI + 16 * mt + 4 * grp);
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) M[mt][nt][jj] = (u[jj] - M[mt][nt][jj]) * ec[jj];
-                }
-            }
-            // X = exp(Gamma_c) X + K^T R'
+            // X <- exp(Gamma_c) X + K^T R',  R' = diag(exp(Gamma_c - Gamma)) R,
+            // R = [0 | Au V] + Aw Z  (Au = Inv diag(beta), Aw = -Inv diag(beta exp Gamma)),
+            // in two halves of 32 token rows so only half of R is live at a time
             const float lam = sLam[0];
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) X[rt][nt] *= lam;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int h = 0; h < 2; ++h) {
+                f32x4 R[2][2];
+#pragma unroll
+                for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) R[m2][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    float zv[2][8];
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) acc_to_perm(Z[2 * kb][nt], Z[2 * kb + 1][nt], zv[nt]);
+                    if constexpr (F32) {
+#pragma unroll
+                        for (int m2 = 0; m2 < 2; ++m2) {
+                            const int mt = 2 * h + m2;
+                            float aw[8];
+                            lds_perm_f(sAwf, LDA, 16 * mt + r16, 32 * kb, grp, aw);
+#pragma unroll
+                            for (int nt = 0; nt < 2; ++nt) R[m2][nt] = mma_f32(aw, zv[nt], R[m2][nt]);
+                            if (isS) {
+                                float au[8];
+                                lds_perm_f(sAuf, LDA, 16 * mt + r16, 32 * kb, grp, au);
+#pragma unroll
+                                for (int nt = 0; nt < 2; ++nt) {
+                                    float vf[8];
+                                    lds_perm_f(sVT, LDT, cbase - D + 16 * nt + r16, 32 * kb, grp, vf);
+                                    R[m2][nt] = mma_f32(au, vf, R[m2][nt]);
+                                }
+                            }
+                        }
+                    } else {
+                        bf16x8 zh[2], zl[2];
+#pragma unroll
+                        for (int nt = 0; nt < 2; ++nt) split8(zv[nt], zh[nt], zl[nt]);
+#pragma unroll
+                        for (int m2 = 0; m2 < 2; ++m2) {
+                            const int mt = 2 * h + m2;
+                            const bf16x8 awh = lds_perm(sAwh, LDA, 16 * mt + r16, 32 * kb, grp);
+                            const bf16x8 awl = lds_perm(sAwl, LDA, 16 * mt + r16, 32 * kb, grp);
+#pragma unroll
+                            for (int nt = 0; nt < 2; ++nt) {
+                                R[m2][nt] = mfma(awh, zh[nt], R[m2][nt]);
+                                R[m2][nt] = mfma(awh, zl[nt], R[m2][nt]);
+                                R[m2][nt] = mfma(awl, zh[nt], R[m2][nt]);
+                            }
+                            if (isS) {
+                                const bf16x8 auh = lds_perm(sAuh, LDA, 16 * mt + r16, 32 * kb, grp);
+                                const bf16x8 aul = lds_perm(sAul, LDA, 16 * mt + r16, 32 * kb, grp);
+#pragma unroll
+                                for (int nt = 0; nt < 2; ++nt) {
+                                    const bf16x8 vb = lds_perm(sVT, LDT, cbase - D + 16 * nt + r16, 32 * kb, grp);
+                                    R[m2][nt] = mfma(auh, vb, R[m2][nt]);
+                                    R[m2][nt] = mfma(aul, vb, R[m2][nt]);
+                                }
+                            }
+                        }
+                    }
+                }
                 float rv[2][8];
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) acc_to_perm(M[2 * kb][nt], M[2 * kb + 1][nt], rv[nt]);
+                for (int m2 = 0; m2 < 2; ++m2) {
+                    const f32x4 ec = *reinterpret_cast<const f32x4 *>(sEc + 16 * (2 * h + m2) + 4 * grp);
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) R[m2][nt] *= ec;
+                }
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) acc_to_perm(R[0][nt], R[1][nt], rv[nt]);
                 if constexpr (F32) {
 #pragma unroll
                     for (int rt = 0; rt < RT; ++rt) {
                         float kf[8];
-                        lds_perm_f(sKT, LDT, 16 * rt + r16, 32 * kb, grp, kf);
+                        lds_perm_f(sKT, LDT, 16 * rt + r16, 32 * h, grp, kf);
 #pragma unroll
                         for (int nt = 0; nt < 2; ++nt) X[rt][nt] = mma_f32(kf, rv[nt], X[rt][nt]);
                     }
@@ -355,7 +436,7 @@ k_build_dense(BuildArgs a) {
                     for (int nt = 0; nt < 2; ++nt) split8(rv[nt], rh[nt], rl[nt]);
 #pragma unroll
                     for (int rt = 0; rt < RT; ++rt) {
-                        const bf16x8 kh = lds_perm(sKT, LDT, 16 * rt + r16, 32 * kb, grp);
+                        const bf16x8 kh = lds_perm(sKT, LDT, 16 * rt + r16, 32 * h, grp);
 #pragma unroll
                         for (int nt = 0; nt < 2; ++nt) {
                             X[rt][nt] = mfma(kh, rh[nt], X[rt][nt]);
