@@ -68,6 +68,25 @@ def compose_cost(n_entries, n_seams, w, d, n_chains, in_bytes):
     return flops * n_chains, byts * n_chains
 
 
+def measured_traffic(key, files):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    passes (profiles/counters.json), or None when the kernel's source changed
+    since they were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    c = json.load(open(path)).get(key)
+    if c is None:
+        return None
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, "state_caching_segment_amd", "csrc", f), "rb").read())
+    if h.hexdigest()[:16] != c["source_sha"]:
+        return None
+    return c["fetch_bytes"] + c["write_bytes"]
+
+
 def cpu_baseline(wl, n_chains_sample, w):
     """The fp64 oracle (build every pair token by token, compose, seams) on a
     sample of chains, all host threads; scaled to request tokens/s for all
@@ -100,6 +119,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c4")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (5 times), to scale HBM counters")
     ap.add_argument("--cpu-chains", type=int, default=-1,
                     help="chains in the oracle's CPU-baseline sample (-1: two per host thread; 0: skip)")
     args = ap.parse_args()
@@ -111,6 +132,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.calib_copy > 0:
+        n = args.calib_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes_read": n * 4, "calib_copy_bytes_written": n * 4, "launches": 5}))
+        return
     hy.load()
 
     wl = workloads.config(args.config, device="cuda")
@@ -172,10 +202,13 @@ def main():
                    "frac": b_hbm / HBM_PEAK} if b_bound == "hbm" else
                   {"bound": "mfma", "achieved": b_mfma / 1e12, "peak": BF16_PEAK / 1e12, "unit": "TFLOP/s",
                    "frac": b_mfma / BF16_PEAK})
-    roof_build.update({"traffic": None, "kernel": "k_build_dense", "alg_bytes": bb, "alg_flops": bf,
+    dense_fam = wl.family in ("deltanet", "gdn", "kda")
+    roof_build.update({"traffic": measured_traffic("build", ["build_dense.hip", "common.h"]) if dense_fam else None,
+                       "kernel": "k_build_dense" if dense_fam else "k_build_diag", "alg_bytes": bb, "alg_flops": bf,
                        "mfma_frac_alg": b_mfma / BF16_PEAK, "hbm_frac_alg": b_hbm / HBM_PEAK})
     roof_comp = {"bound": "hbm", "achieved": cb / tc / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                 "frac": cb / tc / HBM_PEAK, "traffic": None, "kernel": "k_compose_seq", "alg_bytes": cb,
+                 "frac": cb / tc / HBM_PEAK, "traffic": measured_traffic("compose", ["compose.hip", "common.h"]),
+                 "kernel": "k_compose_seq", "alg_bytes": cb,
                  "alg_flops": cf}
     out = {
         "metric": METRIC,
