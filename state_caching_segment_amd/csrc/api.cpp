@@ -139,7 +139,9 @@ int hypic_segment_build(const hypic_layout *L, const hypic_tokens *x, int32_t n_
     if (n_seg == 0) return ok();
     if (!d_seg_begin || !d_seg_end || !d_T || !d_S) return fail(HYPIC_E_INVALID, "NULL segment or output pointer");
     if ((int64_t)n_seg * L->n_chains > 0x7fffffff) return fail(HYPIC_E_INVALID, "n_seg * n_chains too large");
-    if (L->family == HYPIC_KDA) return fail(HYPIC_E_UNSUPPORTED, "KDA pair build is not available in this build");
+    if (L->family == HYPIC_KDA &&
+        (!aligned16(x->g) || ((x->g_tok_stride * esize(L->in_dtype)) & 15) || ((x->g_chain_stride * esize(L->in_dtype)) & 15)))
+        return fail(HYPIC_E_INVALID, "KDA log-gate rows must be 16-byte aligned");
     if (x->tok_stride > (1 << 24)) return fail(HYPIC_E_UNSUPPORTED, "tok_stride above 2^24 elements is not supported");
     hy::BuildArgs a;
     a.x = to_tok(x);
@@ -152,6 +154,7 @@ int hypic_segment_build(const hypic_layout *L, const hypic_tokens *x, int32_t n_
     const int D = padded_d(L->dk);
     const bool bf = L->in_dtype == HYPIC_BF16;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (L->family == HYPIC_KDA) return launched(hy::build_kda(a, bf, D, n_seg, st), "KDA build launch");
     if (dense(L->family)) {
         return launched(hy::build_dense(a, L->family, bf, D, n_seg, st), "dense build launch");
     }

@@ -45,6 +45,7 @@ struct SeamArgs {
 
 // D is the padded state size (32, 64 or 128) the kernel is instantiated for.
 hipError_t build_dense(const BuildArgs &a, int family, bool bf16_in, int D, int n_seg, hipStream_t st);
+hipError_t build_kda(const BuildArgs &a, bool bf16_in, int D, int n_seg, hipStream_t st);
 hipError_t build_diag(const BuildArgs &a, int family, bool bf16_in, int D, int n_seg, hipStream_t st);
 hipError_t compose_seq(const ComposeArgs &a, int family, bool bf16_in, int D, int n_req, hipStream_t st);
 hipError_t seam_advance(const SeamArgs &a, int family, bool bf16_in, int D, int n_items, hipStream_t st);

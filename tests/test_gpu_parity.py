@@ -52,6 +52,11 @@ def test_dense_families(fam, dtype, d):
     check(small(fam, dtype, d))
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 32), ("bf16", 16)])
+def test_kda(dtype, d):
+    check(small("kda", dtype, d))
+
+
 def test_slow_gate_gdn_d128():
     check(small("gdn", "bf16", 128, laws=workloads.SLOW_GDN_LAWS), label="slowgdn_bf16_128")
 
