@@ -117,8 +117,10 @@ int64_t hypic_t_elems(int32_t family, int32_t dk);
 
 /* Device workspace, in bytes, that `op` needs for n_items (segments for
  * BUILD, requests for COMPOSE_*, items for SEAM) with max_len the longest
- * segment (BUILD) or list (COMPOSE_*).  0 means no workspace is needed. */
-size_t hypic_workspace_bytes(const hypic_layout *L, int32_t op, int32_t n_items, int64_t max_len);
+ * segment (BUILD) or list (COMPOSE_*) and seam width w (0: no seams).  0 means
+ * no workspace is needed (every op but HYPIC_OP_COMPOSE_TREE), and also the
+ * answer for invalid arguments.  The workspace holds no state between calls. */
+size_t hypic_workspace_bytes(const hypic_layout *L, int32_t op, int32_t n_items, int64_t max_len, int32_t w);
 
 /*
  * hypic_segment_build -- the cached pair of every segment on every chain.
@@ -153,9 +155,12 @@ int hypic_segment_build(const hypic_layout *L, const hypic_tokens *x, int32_t n_
  *                 fresh request), out = final state
  *   d_o           [n_entries][w][n_chains][dv]; rows of entries without a seam
  *                 are left untouched.  May be NULL when seam == NULL.
- * mode HYPIC_TREE computes the same result through the associative scan
- * (needs a workspace); HYPIC_SEQ needs none.  max_list_len bounds every
- * request's entry count.
+ * mode HYPIC_TREE computes the same result (to rounding) through the
+ * associative scan: blocks of about sqrt(max_list_len) entries are reduced in
+ * parallel, their aggregates scanned, and seam outputs fixed up; it needs a
+ * workspace of hypic_workspace_bytes(L, HYPIC_OP_COMPOSE_TREE, n_req,
+ * max_list_len, w) bytes (HYPIC_E_WORKSPACE if missing or smaller).  HYPIC_SEQ
+ * needs none.  max_list_len must bound every request's entry count.
  */
 int hypic_compose(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t max_list_len,
                   const int32_t *d_list_off, const int32_t *d_pair_id, int64_t n_slots,

@@ -118,11 +118,44 @@ int64_t hypic_t_elems(int32_t family, int32_t dk) {
     return 0;
 }
 
-size_t hypic_workspace_bytes(const hypic_layout *L, int32_t op, int32_t n_items, int64_t max_len) {
-    (void)L;
-    (void)n_items;
-    (void)max_len;
-    if (op == HYPIC_OP_COMPOSE_TREE) return 0;  // the tree scan is not built yet
+}  // extern "C"
+
+namespace {
+
+// Tree-mode blocking: about sqrt(list length) entries per block.
+int tree_block(int max_list) {
+    int b = 1;
+    while (b * b < max_list) ++b;
+    return b < 1 ? 1 : (b > 64 ? 64 : b);
+}
+
+struct TreeLayout {
+    int B, NB;
+    size_t off_aggT, off_aggS, off_sin, off_pvec, total;
+};
+
+TreeLayout tree_layout(const hypic_layout *L, int n_req, int max_list, int w) {
+    TreeLayout t;
+    t.B = tree_block(max_list);
+    t.NB = max_list > 0 ? (max_list + t.B - 1) / t.B : 0;
+    auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t agg = (size_t)n_req * t.NB * L->n_chains * L->dk * L->dk * sizeof(float);
+    const size_t pv = w > 0 ? (size_t)n_req * max_list * w * L->n_chains * L->dk * sizeof(float) : 0;
+    t.off_aggT = 0;
+    t.off_aggS = al(agg);
+    t.off_sin = t.off_aggS + al(agg);
+    t.off_pvec = t.off_sin + al(agg);
+    t.total = t.off_pvec + al(pv);
+    return t;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hypic_workspace_bytes(const hypic_layout *L, int32_t op, int32_t n_items, int64_t max_len, int32_t w) {
+    if (check_layout(L) || n_items < 0 || max_len < 0 || w < 0) return 0;
+    if (op == HYPIC_OP_COMPOSE_TREE) return tree_layout(L, n_items, (int)max_len, w).total;
     return 0;
 }
 
@@ -165,8 +198,6 @@ int hypic_compose(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t ma
                   const int32_t *d_pair_id, int64_t n_slots, const float *d_T, const float *d_S,
                   const hypic_tokens *seam, const int64_t *d_seam_begin, int32_t w, float *d_state, float *d_o,
                   void *d_ws, size_t ws_bytes, void *stream) {
-    (void)d_ws;
-    (void)ws_bytes;
     int rc = check_layout(L);
     if (rc) return rc;
     if (mode != HYPIC_SEQ && mode != HYPIC_TREE) return fail(HYPIC_E_INVALID, "unknown mode %d", mode);
@@ -181,7 +212,6 @@ int hypic_compose(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t ma
         if ((rc = check_tokens(L, seam, true))) return rc;
         if (!d_seam_begin || !d_o) return fail(HYPIC_E_INVALID, "seams need d_seam_begin and d_o");
     }
-    if (mode == HYPIC_TREE) return fail(HYPIC_E_UNSUPPORTED, "tree-mode compose is not available in this build");
     hy::ComposeArgs a;
     a.x = has_seam ? to_tok(seam) : hy::Tok{};
     a.n_chains = L->n_chains;
@@ -196,9 +226,24 @@ int hypic_compose(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t ma
     a.seam_begin = d_seam_begin;
     a.state = d_state;
     a.o = d_o;
-    return launched(hy::compose_seq(a, L->family, L->in_dtype == HYPIC_BF16, padded_d(L->dk), n_req,
-                                    reinterpret_cast<hipStream_t>(stream)),
-                    "compose launch");
+    const bool bf = L->in_dtype == HYPIC_BF16;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (mode == HYPIC_SEQ) return launched(hy::compose_seq(a, L->family, bf, padded_d(L->dk), n_req, st), "compose launch");
+    const TreeLayout tl = tree_layout(L, n_req, max_list_len, has_seam ? w : 0);
+    if (!d_ws || ws_bytes < tl.total)
+        return fail(HYPIC_E_WORKSPACE, "tree compose needs %zu workspace bytes (got %zu)", tl.total, ws_bytes);
+    if (max_list_len == 0) return ok();
+    hy::TreeArgs t;
+    t.c = a;
+    t.B = tl.B;
+    t.NB = tl.NB;
+    t.max_list = max_list_len;
+    char *base = static_cast<char *>(d_ws);
+    t.aggT = reinterpret_cast<float *>(base + tl.off_aggT);
+    t.aggS = reinterpret_cast<float *>(base + tl.off_aggS);
+    t.sin = reinterpret_cast<float *>(base + tl.off_sin);
+    t.pvec = reinterpret_cast<float *>(base + tl.off_pvec);
+    return launched(hy::compose_tree(t, L->family, bf, padded_d(L->dk), n_req, st), "tree compose launch");
 }
 
 int hypic_seam_advance(const hypic_layout *L, const hypic_tokens *x, int32_t n_items, const int64_t *d_tok_begin,

@@ -43,11 +43,23 @@ struct SeamArgs {
     float *o;      // [item][w][chain][dk]
 };
 
+struct TreeArgs {
+    ComposeArgs c;
+    int B;         // entries per block
+    int NB;        // blocks per request (upper bound)
+    int max_list;  // entries per request (upper bound)
+    float *aggT;   // [req][NB][chain][dk][dk] block aggregates
+    float *aggS;
+    float *sin;    // [req][NB][chain][dk][dk] state entering each block
+    float *pvec;   // [req][max_list][w][chain][dk] pulled-back seam queries
+};
+
 // D is the padded state size (32, 64 or 128) the kernel is instantiated for.
 hipError_t build_dense(const BuildArgs &a, int family, bool bf16_in, int D, int n_seg, hipStream_t st);
 hipError_t build_kda(const BuildArgs &a, bool bf16_in, int D, int n_seg, hipStream_t st);
 hipError_t build_diag(const BuildArgs &a, int family, bool bf16_in, int D, int n_seg, hipStream_t st);
 hipError_t compose_seq(const ComposeArgs &a, int family, bool bf16_in, int D, int n_req, hipStream_t st);
+hipError_t compose_tree(const TreeArgs &t, int family, bool bf16_in, int D, int n_req, hipStream_t st);
 hipError_t seam_advance(const SeamArgs &a, int family, bool bf16_in, int D, int n_items, hipStream_t st);
 
 }  // namespace hy

@@ -61,7 +61,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.hypic_t_elems.argtypes = [i32, i32]
     lib.hypic_t_elems.restype = i64
-    lib.hypic_workspace_bytes.argtypes = [P, i32, i32, i64]
+    lib.hypic_workspace_bytes.argtypes = [P, i32, i32, i64, i32]
     lib.hypic_workspace_bytes.restype = sz
     lib.hypic_segment_build.argtypes = [P, P, i32, P, P, i64, P, P, P, sz, P]
     lib.hypic_segment_build.restype = ctypes.c_int
@@ -121,8 +121,8 @@ def hypic_t_elems(family: str, dk: int) -> int:
     return int(load().hypic_t_elems(FAMILY[family], dk))
 
 
-def hypic_workspace_bytes(L: hypic_layout, op: int, n_items: int, max_len: int) -> int:
-    return int(load().hypic_workspace_bytes(ctypes.byref(L), op, n_items, max_len))
+def hypic_workspace_bytes(L: hypic_layout, op: int, n_items: int, max_len: int, w: int = 0) -> int:
+    return int(load().hypic_workspace_bytes(ctypes.byref(L), op, n_items, max_len, w))
 
 
 def hypic_segment_build(L: hypic_layout, x: hypic_tokens, n_seg: int, seg_begin, seg_end, max_seg_len: int,

@@ -20,8 +20,10 @@ FLOOR = 2.0 ** -100
 TOL = {"f32": 1e-4, "bf16": 5e-3}
 
 
-def gpu_request(wl, w=None, stream=None):
-    """Build every segment body's pair, then compose each request with its seams."""
+def gpu_request(wl, w=None, stream=None, mode=None):
+    """Build every segment body's pair, then compose each request with its seams
+    (sequential compose, or the tree scan with mode=hy.TREE)."""
+    mode = hy.SEQ if mode is None else mode
     w = wl.w if w is None else w
     plan = request_plan(wl.requests, w)
     dev = wl.k.device
@@ -38,8 +40,12 @@ def gpu_request(wl, w=None, stream=None):
     lo = torch.from_numpy(plan.list_off).to(dev)
     pid = torch.from_numpy(plan.pair_id).to(dev)
     seam = torch.from_numpy(plan.seam_begin).to(dev)
-    hy.hypic_compose(L, hy.SEQ, plan.n_req, plan.max_list_len, lo, pid, plan.n_slots, T, S,
-                     x if w > 0 else None, seam, w, state, o, stream=stream)
+    ws, nws = None, 0
+    if mode == hy.TREE:
+        nws = hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, plan.n_req, plan.max_list_len, w)
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    hy.hypic_compose(L, mode, plan.n_req, plan.max_list_len, lo, pid, plan.n_slots, T, S,
+                     x if w > 0 else None, seam, w, state, o, ws, nws, stream=stream)
     torch.cuda.synchronize()
     return {"plan": plan, "T": T, "S": S, "state": state, "O": o}
 

@@ -98,7 +98,7 @@ def test_compose_and_seam_validation():
     xq = _fake_tokens("gdn", cs=64)
     xq.q = None
     expect(-1, c, L, hy.SEQ, 1, 2, 8, 8, 2, 8, 8, xq, 8, 8, 8, 8)              # seams need q
-    expect(-2, c, L, hy.TREE, 1, 2, 8, 8, 2, 8, 8, None, None, 0, 8, None)     # not built
+    expect(-3, c, L, hy.TREE, 1, 2, 8, 8, 2, 8, 8, None, None, 0, 8, None)     # tree needs a workspace
     c(L, hy.SEQ, 0, 0, None, None, 0, None, None, None, None, 0, None, None)   # empty: OK
     s = hy.hypic_seam_advance
     expect(-1, s, L, x, 2, None, 8, 8, 8)
@@ -108,8 +108,15 @@ def test_compose_and_seam_validation():
 
 def test_workspace_query():
     L = hy.layout("gdn", "bf16", 4, 128)
-    assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_SEQ, 4, 48) == 0
-    assert hy.hypic_workspace_bytes(L, hy.OP_BUILD, 4, 48) == 0
+    assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_SEQ, 4, 48, 8) == 0
+    assert hy.hypic_workspace_bytes(L, hy.OP_BUILD, 4, 48, 8) == 0
+    # tree: 3 block-aggregate arrays of n_req x ceil(48/7) x chains x dk^2 fp32, plus seam queries
+    nb, agg = 7, 4 * 7 * 4 * 128 * 128 * 4
+    pv = 4 * 48 * 8 * 4 * 128 * 4
+    assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 4, 48, 8) == 3 * agg + pv
+    assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 4, 48, 0) == 3 * agg
+    assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 4, 48, -1) == 0
+    assert hy.hypic_workspace_bytes(hy.layout("gdn", "bf16", 4, 100), hy.OP_COMPOSE_TREE, 4, 48, 8) == 0
 
 
 def test_request_plan():

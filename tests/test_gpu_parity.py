@@ -30,9 +30,9 @@ def small(fam, dtype, d, n_chains=4, lens=RAGGED, laws=None, cid=40, w=8):
                           lens=lens, w=w, laws=laws, gamma=gamma, device="cuda")
 
 
-def check(wl, chains=None, w=None, label=""):
+def check(wl, chains=None, w=None, label="", mode=None):
     chains = list(range(wl.n_chains)) if chains is None else chains
-    gpu = gpu_request(wl, w=w)
+    gpu = gpu_request(wl, w=w, mode=mode)
     ref = oracle_request(wl, chains, w=w)
     err = compare(wl, gpu, ref, chains, w=w)
     print(label or wl.name, {k: (f"{v:.2e}" if isinstance(v, float) else v) for k, v in err.items()}, flush=True)
@@ -55,6 +55,21 @@ def test_dense_families(fam, dtype, d):
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 32), ("bf16", 16)])
 def test_kda(dtype, d):
     check(small("kda", dtype, d))
+
+
+@pytest.mark.parametrize("fam,dtype,d", [("gdn", "bf16", 128), ("kda", "bf16", 128), ("gla", "bf16", 64),
+                                         ("retnet", "f32", 32), ("deltanet", "f32", 16), ("mamba2", "bf16", 64),
+                                         ("linear", "f32", 64)])
+def test_tree_compose(fam, dtype, d):
+    """Tree-scan compose (several requests of unequal length, lists not a
+    multiple of the block size) against the oracle's left-to-right path."""
+    lens = [[70, 40, 33, 90, 25, 61, 44, 30, 52, 19, 27], [130, 60, 45], [50], [40, 31, 29, 66, 73, 20, 18]]
+    laws = {"gdn": workloads.GDN_LAWS, "deltanet": workloads.GDN_LAWS, "kda": workloads.KDA_LAWS}.get(
+        fam, workloads.DIAG_LAWS)
+    wl = workloads.make(f"tree_{fam}", config_id=77, family=fam, dtype=dtype, n_chains=3, d=d, lens=lens, w=8,
+                        laws=laws, gamma=workloads.retnet_gammas(3) if fam == "retnet" else None, device="cuda")
+    check(wl, mode=hy.TREE, label=f"tree_{fam}_{dtype}_{d}")
+    check(wl, mode=hy.TREE, w=0, label=f"tree_{fam}_{dtype}_{d}_w0")
 
 
 def test_slow_gate_gdn_d128():
