@@ -68,6 +68,18 @@ def compose_cost(n_entries, n_seams, w, d, n_chains, in_bytes):
     return flops * n_chains, byts * n_chains
 
 
+def build_kernel(family, dtype):
+    """The build kernel the library dispatches for a family and input dtype,
+    and the sources whose hash keys its stored counter readings."""
+    if family == "kda":
+        return "k_build_kda", ["build_kda.hip", "common.h"]
+    if family in ("deltanet", "gdn"):
+        if dtype == "bf16":
+            return "k_build_dense_pipe", ["build_dense_pipe.hip", "common.h"]
+        return "k_build_dense", ["build_dense.hip", "common.h"]
+    return "k_build_diag", ["build_diag.hip", "common.h"]
+
+
 def measured_traffic(key, files):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     passes (profiles/counters.json), or None when the kernel's source changed
@@ -202,9 +214,9 @@ def main():
                    "frac": b_hbm / HBM_PEAK} if b_bound == "hbm" else
                   {"bound": "mfma", "achieved": b_mfma / 1e12, "peak": BF16_PEAK / 1e12, "unit": "TFLOP/s",
                    "frac": b_mfma / BF16_PEAK})
-    dense_fam = wl.family in ("deltanet", "gdn", "kda")
-    roof_build.update({"traffic": measured_traffic("build", ["build_dense.hip", "common.h"]) if dense_fam else None,
-                       "kernel": "k_build_dense" if dense_fam else "k_build_diag", "alg_bytes": bb, "alg_flops": bf,
+    bk_name, bk_files = build_kernel(wl.family, wl.dtype)
+    roof_build.update({"traffic": measured_traffic("build", bk_files),
+                       "kernel": bk_name, "alg_bytes": bb, "alg_flops": bf,
                        "mfma_frac_alg": b_mfma / BF16_PEAK, "hbm_frac_alg": b_hbm / HBM_PEAK})
     roof_comp = {"bound": "hbm", "achieved": cb / tc / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                  "frac": cb / tc / HBM_PEAK, "traffic": measured_traffic("compose", ["compose.hip", "common.h"]),

@@ -189,6 +189,7 @@ int hypic_segment_build(const hypic_layout *L, const hypic_tokens *x, int32_t n_
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (L->family == HYPIC_KDA) return launched(hy::build_kda(a, bf, D, n_seg, st), "KDA build launch");
     if (dense(L->family)) {
+        if (bf) return launched(hy::build_dense_pipe(a, L->family, D, n_seg, st), "dense build launch");
         return launched(hy::build_dense(a, L->family, bf, D, n_seg, st), "dense build launch");
     }
     return launched(hy::build_diag(a, L->family, bf, D, n_seg, st), "diagonal build launch");

@@ -1,0 +1,487 @@
+// Dense-transition pair build (DeltaNet, Gated DeltaNet), bf16 inputs, for
+// gfx950: the chunk factors of chunk j+1 are formed while chunk j is carried.
+//
+// Same method and chunk form as k_build_dense (HYPIC, codernav.top article,
+// section on linear layers: the cached pair (T_C, S(C|0))): for a chunk of
+// c = 64 tokens with chunk-local cumulative log-decay Gamma and
+// N = diag(beta) tril(G, -1), G_ti = (k_t . k_i) e^{Gamma_t - Gamma_i},
+//     Y  = [0 | V] - diag(e^Gamma) K X
+//     R  = (I + N)^-1 diag(beta) Y
+//     X <- e^{Gamma_c} X + K^T diag(e^{Gamma_c - Gamma}) R
+// on X = [T | S] from [I | 0].  R is found by blocked forward substitution in
+// 16-row blocks, R_b = (I + N_bb)^-1 (diag(beta) Y_b - sum_{c<b} N_bc R_c),
+// so only the four diagonal 16 x 16 inverses are ever formed.
+//
+// Workgroup = 2d/32 carry waves + 2 factor waves, one (segment, chain) each.
+//   carry wave w: columns 32w .. 32w+31 of X, resident in MFMA accumulators;
+//     per chunk Z = K X, Y, the substitution (16x16x16 MFMAs whose B operand
+//     is an accumulator tile as it stands) and the X update.  K^T and V tiles
+//     come from transpose reads of the row-major K and V rows in LDS.
+//   factor wave 0: stages K of the next chunk, scans the gates (DPP), forms
+//     the Gram tiles on the matrix cores, writes the off-diagonal blocks of -N
+//     pre-split into hi + lo bf16 in the layout the carry waves read as MFMA
+//     A operands, and inverts the four diagonal blocks (one row per lane, one
+//     block per lane group).  It works alone, so its steps
+//     need no workgroup barrier.
+//   factor wave 1: stages V of the next chunk.
+// Chunk inputs are prefetched two chunks ahead into the factor waves'
+// registers; the factors live in a double-buffered LDS area; the workgroup
+// meets at one barrier per chunk.
+//
+// Precision: keys and values are exact in bf16; every other operand is split
+// into hi + lo bf16 (two or three passes, fp32 accumulation, fp32 state).
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace hy {
+
+typedef short s4 __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct PipeCfg {
+    static constexpr int NC = 2 * D / 32;  // carry waves
+    static constexpr int NT = (NC + 2) * 64;
+    static constexpr int RT = D / 16;
+    static constexpr int KB = D / 32;
+    static constexpr int LDK = D + 8;  // bf16 row stride of K and V rows
+    static constexpr int LDT = 20;     // fp32 row stride of a diagonal block of N
+    static constexpr int TILE = 512;   // bf16 per pre-split 16 x 16 tile: [row][4 col groups][hi 4 | lo 4]
+    static constexpr int al(int x) { return (x + 15) / 16 * 16; }
+    // one buffer: K rows, V rows, -N off-diagonal tiles, diagonal inverses,
+    // beta, e^Gamma, e^{Gc-Gamma}, e^Gc
+    static constexpr int bK = 0;
+    static constexpr int bV = bK + al(CH * LDK * 2);
+    static constexpr int bNo = bV + al(CH * LDK * 2);
+    static constexpr int bID = bNo + 6 * TILE * 2;
+    static constexpr int bBeta = bID + 4 * TILE * 2;
+    static constexpr int bEg = bBeta + CH * 4;
+    static constexpr int bEc = bEg + CH * 4;
+    static constexpr int bLam = bEc + CH * 4;
+    static constexpr int BUF = al(bLam + 16);
+    // factor-wave scratch: Gamma (log2 units), diagonal blocks of N
+    static constexpr int offG = 2 * BUF;
+    static constexpr int offNt = offG + CH * 4;
+    static constexpr int total = offNt + 4 * 16 * LDT * 4;
+    static_assert(total <= 160 * 1024, "LDS budget");
+};
+
+// 4 consecutive rows k0 .. k0+3 of column c0 + r16 of a row-major bf16 LDS
+// matrix (all 16 lanes of a lane group pass the same k0 and c0): the gfx950
+// transpose read, where source lane 4m + q supplies row k0 + m, columns
+// c0 + 4q .. c0 + 4q + 3.
+__device__ __forceinline__ bf16x4 lds_tr4(const bf16 *M, int ld, int k0, int c0, int r16) {
+    const bf16 *p = M + (k0 + (r16 >> 2)) * ld + c0 + 4 * (r16 & 3);
+    const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4 *)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+// permuted-k A fragment of row-major M transposed: rows = columns c0 + r16 of
+// M, k = rows kbase + {4grp .. 4grp+3, 16+4grp .. 16+4grp+3}
+__device__ __forceinline__ bf16x8 lds_tr_perm(const bf16 *M, int ld, int kbase, int c0, int r16, int grp) {
+    const bf16x4 a = lds_tr4(M, ld, kbase + 4 * grp, c0, r16);
+    const bf16x4 b = lds_tr4(M, ld, kbase + 16 + 4 * grp, c0, r16);
+    bf16x8 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+    r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+    return r;
+}
+
+typedef short s8v __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ void split4(const f32x4 &x, s4 &h, s4 &l) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bf16 y = (bf16)x[e];
+        h[e] = __builtin_bit_cast(short, y);
+        l[e] = __builtin_bit_cast(short, (bf16)(x[e] - (float)y));
+    }
+}
+
+// C += A B on v_mfma_f32_16x16x16_bf16, operands split hi + lo (hi.hi + hi.lo +
+// lo.hi).  A: lane holds A[r16][4grp + e]; B: B[4grp + e][r16], which is how a
+// 16 x 16 accumulator tile sits in the lanes.
+__device__ __forceinline__ f32x4 mma16(const s4 &ah, const s4 &al, const s4 &bh, const s4 &bl, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, c, 0, 0, 0);
+    return c;
+}
+
+// A fragment of a pre-split tile: 16 bytes per lane, [hi 4 | lo 4]
+__device__ __forceinline__ void tile_frag(const bf16 *t, int r16, int grp, s4 &h, s4 &l) {
+    const s8v v = *reinterpret_cast<const s8v *>(t + (r16 * 4 + grp) * 8);
+    h = __builtin_shufflevector(v, v, 0, 1, 2, 3);
+    l = __builtin_shufflevector(v, v, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ void tile_put(bf16 *t, int row, int q, const f32x4 &x) {
+    s4 h, l;
+    split4(x, h, l);
+    *reinterpret_cast<s8v *>(t + (row * 4 + q) * 8) = __builtin_shufflevector(h, l, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int CTRL, int ROWS, bool ZERO>
+__device__ __forceinline__ float dpp_take(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xf, ZERO));
+}
+
+// inclusive prefix sum over the 64 lanes: shifts within rows of 16, then the
+// row totals carried forward by the row broadcasts of lanes 15 and 31
+__device__ __forceinline__ float wave_incl_scan(float v) {
+    v += dpp_take<0x111, 0xf, true>(v);  // row_shr:1
+    v += dpp_take<0x112, 0xf, true>(v);  // row_shr:2
+    v += dpp_take<0x114, 0xf, true>(v);  // row_shr:4
+    v += dpp_take<0x118, 0xf, true>(v);  // row_shr:8
+    v += dpp_take<0x142, 0xa, false>(v); // row_bcast:15 into rows 1, 3
+    v += dpp_take<0x143, 0xc, false>(v); // row_bcast:31 into rows 2, 3
+    return v;
+}
+
+// keep the compiler from moving LDS accesses across a point where another lane
+// of the same wave reads what this one wrote (the wave's LDS ops run in order)
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int D, int FAM>
+__global__ void __launch_bounds__((2 * D / 32 + 2) * 64)
+k_build_dense_pipe(BuildArgs a) {
+    using Cfg = PipeCfg<D>;
+    constexpr int NC = Cfg::NC, RT = Cfg::RT, KB = Cfg::KB;
+    constexpr int LDK = Cfg::LDK, LDT = Cfg::LDT, TILE = Cfg::TILE;
+    constexpr float L2E = 1.4426950408889634f;
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::total];
+    float *sGam = reinterpret_cast<float *>(smem + Cfg::offG);
+    float *sNt = reinterpret_cast<float *>(smem + Cfg::offNt);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform role
+    const int r16 = lane & 15, grp = lane >> 4;
+    const int seg = blockIdx.x / a.n_chains, chain = blockIdx.x % a.n_chains;
+    const int dk = a.dk;
+    const int64_t b0 = a.seg_begin[seg], n = a.seg_end[seg] - b0;
+    const int nch = (int)((n + CH - 1) / CH);
+    const bf16 *kp = reinterpret_cast<const bf16 *>(a.x.k) + (int64_t)chain * a.x.cs;
+    const bf16 *vp = reinterpret_cast<const bf16 *>(a.x.v) + (int64_t)chain * a.x.cs;
+    const bf16 *gp = FAM == GDN ? reinterpret_cast<const bf16 *>(a.x.g) + (int64_t)chain * a.x.gcs : nullptr;
+    const bf16 *bp = reinterpret_cast<const bf16 *>(a.x.beta) + (int64_t)chain * a.x.bcs;
+
+    const bool carry = wv < NC;
+    const int cbase = wv * 32;
+    const bool isS = carry && cbase >= D;
+
+    // Carry waves and factor waves run separate loops that meet at the same
+    // number of barriers: (nch > 0) + nch.
+    if (!carry) {
+    // the factor waves go first at issue on the SIMDs they share with carry
+    // waves: their chain of short dependent steps sets the chunk period
+    __builtin_amdgcn_s_setprio(3);
+    // prefetched token row `lane` of a chunk: D bf16 = D/8 16-byte pieces
+    constexpr int RV = D / 8;
+    bf16x8 pre[RV];
+    auto pre_put = [&](int p, const bf16x8 &v) { pre[p] = v; };
+    auto pre_get = [&](int p) { return pre[p]; };
+    bf16 gpre = (bf16)0.f, bpre = (bf16)0.f;
+    auto prefetch = [&](int c) {
+        const int64_t c0 = (int64_t)c * CH;
+        const int L = (int)(n - c0 < CH ? n - c0 : CH);
+        const int64_t t = b0 + c0 + lane;
+        const bf16 *src = (wv == NC ? kp : vp) + t * a.x.ts;
+#pragma unroll
+        for (int p = 0; p < RV; ++p) {
+            bf16x8 v;
+            if (lane < L && 8 * p < dk) {
+                v = *reinterpret_cast<const bf16x8 *>(src + 8 * p);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = (bf16)0.f;
+            }
+            pre_put(p, v);
+        }
+        if (wv == NC) {
+            gpre = bpre = (bf16)0.f;
+            if (lane < L) {
+                if (FAM == GDN) gpre = gp[t * a.x.gts];
+                bpre = bp[t * a.x.bts];
+            }
+        }
+    };
+    // factor-wave work for chunk c into buffer c & 1
+    auto factors = [&](int c) {
+        // lane-derived addresses are rebuilt here from an opaque copy of the
+        // lane id rather than held in registers across the chunk loop
+        int lane = tid & 63;
+        asm volatile("" : "+v"(lane));
+        const int r16 = lane & 15, grp = lane >> 4;
+        char *buf = smem + (c & 1) * Cfg::BUF;
+        bf16 *bK = reinterpret_cast<bf16 *>(buf + Cfg::bK);
+        if (wv == NC + 1) {
+            bf16 *bV = reinterpret_cast<bf16 *>(buf + Cfg::bV);
+#pragma unroll
+            for (int p = 0; p < RV; ++p) *reinterpret_cast<bf16x8 *>(bV + lane * LDK + 8 * p) = pre_get(p);
+            return;
+        }
+        bf16 *bNo = reinterpret_cast<bf16 *>(buf + Cfg::bNo);
+        bf16 *bID = reinterpret_cast<bf16 *>(buf + Cfg::bID);
+        float *bBeta = reinterpret_cast<float *>(buf + Cfg::bBeta);
+        float *bEg = reinterpret_cast<float *>(buf + Cfg::bEg);
+        float *bEc = reinterpret_cast<float *>(buf + Cfg::bEc);
+        float *bLam = reinterpret_cast<float *>(buf + Cfg::bLam);
+        // K rows; gate scan (lane = token), Gamma kept in log2 units
+#pragma unroll
+        for (int p = 0; p < RV; ++p) *reinterpret_cast<bf16x8 *>(bK + lane * LDK + 8 * p) = pre_get(p);
+        {
+            float s = 0.f, gc = 0.f;
+            if (FAM == GDN) {
+                s = wave_incl_scan((float)gpre * L2E);
+                gc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 63));
+            }
+            sGam[lane] = s;
+            bBeta[lane] = (float)bpre;
+            bEg[lane] = __builtin_amdgcn_exp2f(s);
+            bEc[lane] = __builtin_amdgcn_exp2f(gc - s);
+            if (lane == 0) bLam[0] = __builtin_amdgcn_exp2f(gc);
+        }
+        wave_lds_fence();
+        // Gram tiles, one block row b at a time.  Off-diagonal (b > c): the
+        // lane holds row t = 16b + r16, columns i = 16c + 4grp + e of -N (G is
+        // symmetric, so K_c K_b^T in C layout is that), stored pre-split.
+        // Diagonal: the lane holds rows t = 16b + 4grp + e, column i = 16b + r16,
+        // stored row-major in fp32 for the inverse below.
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            f32x4 acc[4];
+#pragma unroll
+            for (int nt = 0; nt <= mt; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const bf16x8 km = lds_cont(bK, LDK, 16 * mt + r16, 32 * kb, grp);
+#pragma unroll
+                for (int nt = 0; nt < mt; ++nt)
+                    acc[nt] = mfma(lds_cont(bK, LDK, 16 * nt + r16, 32 * kb, grp), km, acc[nt]);
+                acc[mt] = mfma(km, km, acc[mt]);
+            }
+            const float gt = sGam[16 * mt + r16], bt = bBeta[16 * mt + r16];
+#pragma unroll
+            for (int nt = 0; nt < mt; ++nt) {
+                const f32x4 gi = *reinterpret_cast<const f32x4 *>(sGam + 16 * nt + 4 * grp);
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = -bt * acc[nt][e];
+                    if (FAM == GDN) v[e] *= __builtin_amdgcn_exp2f(gt - gi[e]);
+                }
+                tile_put(bNo + (mt * (mt - 1) / 2 + nt) * TILE, r16, grp, v);
+            }
+            const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sGam + 16 * mt + 4 * grp);
+            const f32x4 b4 = *reinterpret_cast<const f32x4 *>(bBeta + 16 * mt + 4 * grp);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float x = b4[e] * acc[mt][e];
+                if (FAM == GDN) x *= __builtin_amdgcn_exp2f(g4[e] - gt);
+                sNt[(16 * mt + 4 * grp + e) * LDT + r16] = (4 * grp + e > r16) ? x : 0.f;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        wave_lds_fence();
+        // row r16 of (I + N_bb)^-1 for block b = grp: y (I + N_bb) = e_r.  Swept
+        // from the last row up: once y_i is final its multiple of row i of N_bb
+        // leaves every y_j, j < i, so the dependent chain is 16 steps long.
+        {
+            float y[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) y[j] = (j == r16) ? 1.f : 0.f;
+            // row i of N_bb is read one step ahead of its use
+            f32x4 cur[4], nxt[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) cur[q] = *reinterpret_cast<const f32x4 *>(sNt + (16 * grp + 15) * LDT + 4 * q);
+#pragma unroll
+            for (int i = 15; i > 0; --i) {
+#pragma unroll
+                for (int q = 0; 4 * q < i - 1; ++q)
+                    nxt[q] = *reinterpret_cast<const f32x4 *>(sNt + (16 * grp + i - 1) * LDT + 4 * q);
+#pragma unroll
+                for (int q = 0; 4 * q < i; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * q + e < i) y[4 * q + e] -= y[i] * cur[q][e];
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                tile_put(bID + grp * TILE, r16, q, f32x4{y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]});
+        }
+    };
+    if (nch > 0) {
+        prefetch(0);
+        factors(0);
+        if (nch > 1) prefetch(1);
+        __syncthreads();
+    }
+    for (int c = 0; c < nch; ++c) {
+        if (c + 1 < nch) {
+            factors(c + 1);
+            if (c + 2 < nch) prefetch(c + 2);
+        }
+        __syncthreads();
+    }
+    return;
+    }
+
+    f32x4 X[RT][2];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) X[rt][nt][jj] = (16 * rt + 4 * grp + jj == cbase + 16 * nt + r16) ? 1.f : 0.f;
+    if (nch > 0) __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+        {
+            const char *buf = smem + (c & 1) * Cfg::BUF;
+            const bf16 *bK = reinterpret_cast<const bf16 *>(buf + Cfg::bK);
+            const bf16 *bV = reinterpret_cast<const bf16 *>(buf + Cfg::bV);
+            const bf16 *bNo = reinterpret_cast<const bf16 *>(buf + Cfg::bNo);
+            const bf16 *bID = reinterpret_cast<const bf16 *>(buf + Cfg::bID);
+            const float *bBeta = reinterpret_cast<const float *>(buf + Cfg::bBeta);
+            const float *bEg = reinterpret_cast<const float *>(buf + Cfg::bEg);
+            const float *bEc = reinterpret_cast<const float *>(buf + Cfg::bEc);
+            const float lam = *reinterpret_cast<const float *>(buf + Cfg::bLam);
+            // Z = K X
+            f32x4 Z[4][2];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) Z[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                bf16x8 xh[2], xl[2];
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    float xv[8];
+                    acc_to_perm(X[2 * kb][nt], X[2 * kb + 1][nt], xv);
+                    split8(xv, xh[nt], xl[nt]);
+                }
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    const bf16x8 kh = lds_perm(bK, LDK, 16 * mt + r16, 32 * kb, grp);
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        Z[mt][nt] = mfma(kh, xh[nt], Z[mt][nt]);
+                        Z[mt][nt] = mfma(kh, xl[nt], Z[mt][nt]);
+                    }
+                }
+            }
+            // diag(beta) Y = diag(beta) ([0 | V] - diag(e^Gamma) Z), in Z
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const f32x4 eg = *reinterpret_cast<const f32x4 *>(bEg + 16 * mt + 4 * grp);
+                const f32x4 bt = *reinterpret_cast<const f32x4 *>(bBeta + 16 * mt + 4 * grp);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) Z[mt][nt][jj] = -Z[mt][nt][jj] * eg[jj];
+                    if (isS) {
+                        const bf16x4 v4 = lds_tr4(bV, LDK, 16 * mt + 4 * grp, cbase - D + 16 * nt, r16);
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) Z[mt][nt][jj] += (float)v4[jj];
+                    }
+                    Z[mt][nt] *= bt;
+                }
+            }
+            // R_b = (I + N_bb)^-1 (diag(beta) Y_b - sum_{c<b} N_bc R_c), R_b replacing Y_b;
+            // the split R blocks are kept for the blocks below them
+            s4 Rh[3][2], Rl[3][2];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+#pragma unroll
+                for (int c2 = 0; c2 < b; ++c2) {
+                    s4 nh, nl;
+                    tile_frag(bNo + (b * (b - 1) / 2 + c2) * TILE, r16, grp, nh, nl);
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) Z[b][nt] = mma16(nh, nl, Rh[c2][nt], Rl[c2][nt], Z[b][nt]);
+                }
+                s4 ih, il;
+                tile_frag(bID + b * TILE, r16, grp, ih, il);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    s4 yh, yl;
+                    split4(Z[b][nt], yh, yl);
+                    Z[b][nt] = mma16(ih, il, yh, yl, f32x4{0.f, 0.f, 0.f, 0.f});
+                    if (b < 3) split4(Z[b][nt], Rh[b][nt], Rl[b][nt]);
+                }
+            }
+            // X = e^{Gamma_c} X + K^T diag(e^{Gamma_c - Gamma}) R
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) X[rt][nt] *= lam;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const f32x4 ec = *reinterpret_cast<const f32x4 *>(bEc + 16 * mt + 4 * grp);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) Z[mt][nt] *= ec;
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                bf16x8 rh[2], rl[2];
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    float rv[8];
+                    acc_to_perm(Z[2 * h][nt], Z[2 * h + 1][nt], rv);
+                    split8(rv, rh[nt], rl[nt]);
+                }
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    const bf16x8 kt = lds_tr_perm(bK, LDK, 32 * h, 16 * rt, r16, grp);
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        X[rt][nt] = mfma(kt, rh[nt], X[rt][nt]);
+                        X[rt][nt] = mfma(kt, rl[nt], X[rt][nt]);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    {
+        float *To = a.T + ((int64_t)seg * a.n_chains + chain) * dk * dk;
+        float *So = a.S + ((int64_t)seg * a.n_chains + chain) * dk * dk;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int row = 16 * rt + 4 * grp + jj;
+                    const int col = cbase + 16 * nt + r16 - (isS ? D : 0);
+                    if (row < dk && col < dk) (isS ? So : To)[row * dk + col] = X[rt][nt][jj];
+                }
+    }
+}
+
+template <int D, int FAM>
+static hipError_t launch_pipe(const BuildArgs &a, int n_seg, hipStream_t st) {
+    const dim3 grid((unsigned)(n_seg * (int64_t)a.n_chains));
+    hipLaunchKernelGGL((k_build_dense_pipe<D, FAM>), grid, dim3(PipeCfg<D>::NT), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t build_dense_pipe(const BuildArgs &a, int family, int D, int n_seg, hipStream_t st) {
+    if (family != GDN && family != DELTANET) return hipErrorInvalidValue;
+    switch (D) {
+    case 32: return family == GDN ? launch_pipe<32, GDN>(a, n_seg, st) : launch_pipe<32, DELTANET>(a, n_seg, st);
+    case 64: return family == GDN ? launch_pipe<64, GDN>(a, n_seg, st) : launch_pipe<64, DELTANET>(a, n_seg, st);
+    case 128: return family == GDN ? launch_pipe<128, GDN>(a, n_seg, st) : launch_pipe<128, DELTANET>(a, n_seg, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace hy

@@ -56,6 +56,7 @@ struct TreeArgs {
 
 // D is the padded state size (32, 64 or 128) the kernel is instantiated for.
 hipError_t build_dense(const BuildArgs &a, int family, bool bf16_in, int D, int n_seg, hipStream_t st);
+hipError_t build_dense_pipe(const BuildArgs &a, int family, int D, int n_seg, hipStream_t st);
 hipError_t build_kda(const BuildArgs &a, bool bf16_in, int D, int n_seg, hipStream_t st);
 hipError_t build_diag(const BuildArgs &a, int family, bool bf16_in, int D, int n_seg, hipStream_t st);
 hipError_t compose_seq(const ComposeArgs &a, int family, bool bf16_in, int D, int n_req, hipStream_t st);
