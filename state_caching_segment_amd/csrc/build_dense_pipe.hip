@@ -1,29 +1,32 @@
 // Dense-transition pair build (DeltaNet, Gated DeltaNet), bf16 inputs, for
 // gfx950: the chunk factors of chunk j+1 are formed while chunk j is carried.
 //
-// Same method and chunk form as k_build_dense (HYPIC, codernav.top article,
-// section on linear layers: the cached pair (T_C, S(C|0))): for a chunk of
-// c = 64 tokens with chunk-local cumulative log-decay Gamma and
-// N = diag(beta) tril(G, -1), G_ti = (k_t . k_i) e^{Gamma_t - Gamma_i},
-//     Y  = [0 | V] - diag(e^Gamma) K X
-//     R  = (I + N)^-1 diag(beta) Y
-//     X <- e^{Gamma_c} X + K^T diag(e^{Gamma_c - Gamma}) R
-// on X = [T | S] from [I | 0].  R is found by blocked forward substitution in
-// 16-row blocks, R_b = (I + N_bb)^-1 (diag(beta) Y_b - sum_{c<b} N_bc R_c),
-// so only the four diagonal 16 x 16 inverses are ever formed.
+// Method: HYPIC (codernav.top article, section on linear layers: the cached
+// pair (T_C, S(C|0))), advanced in chunks of c = 64 tokens on X = [T | S] from
+// [I | 0].  With chunk-local cumulative log-gates Gamma_t, lambda = e^{Gamma_c},
+// E = diag(e^{Gamma_c - Gamma_t}) and the undecayed strictly lower
+// N0 = diag(beta) tril(K K^T, -1), the decayed chunk system is the similarity
+// transform E^-1 (I + N0) E of the undecayed one, so per chunk
+//     Y  = [0 | E V] - lambda K X
+//     R' = (I + N0)^-1 diag(beta) Y          (R' = E R of the decayed form)
+//     X <- lambda X + K^T R'
+// and no exponent appears inside the chunk system.  R' is found by blocked
+// forward substitution in 16-row blocks,
+//     R'_b = A_b Y_b - sum_{c<b} M_bc R'_c,   A_b = (I + N0_bb)^-1 diag(beta_b),
+//                                             M_bc = (I + N0_bb)^-1 N0_bc.
 //
 // Workgroup = 2d/32 carry waves + 2 factor waves, one (segment, chain) each.
 //   carry wave w: columns 32w .. 32w+31 of X, resident in MFMA accumulators;
-//     per chunk Z = K X, Y, the substitution (16x16x16 MFMAs whose B operand
-//     is an accumulator tile as it stands) and the X update.  K^T and V tiles
-//     come from transpose reads of the row-major K and V rows in LDS.
-//   factor wave 0: stages K of the next chunk, scans the gates (DPP), forms
-//     the Gram tiles on the matrix cores, writes the off-diagonal blocks of -N
-//     pre-split into hi + lo bf16 in the layout the carry waves read as MFMA
-//     A operands, and inverts the four diagonal blocks (one row per lane, one
-//     block per lane group).  It works alone, so its steps
-//     need no workgroup barrier.
-//   factor wave 1: stages V of the next chunk.
+//     per chunk Z = K X, Y, the block solve (16x16x16 MFMAs whose B operand is
+//     an accumulator tile as it stands) and the X update.  K^T comes from
+//     transpose reads of the row-major K rows in LDS.
+//   factor wave 0: stages K of the next chunk, forms the Gram tiles on the
+//     matrix cores, inverts the four diagonal blocks (one row per lane, one
+//     block per lane group) and forms A_b and M_bc, written pre-split into
+//     hi + lo bf16 in the layout the carry waves read as MFMA A operands.
+//   factor wave 1: scans the gates (DPP) and stages E V of the next chunk in
+//     fp32, transposed, so an S wave reads its Y tile in one 16-byte load.
+// Each factor wave works alone, so its steps need no workgroup barrier.
 // Chunk inputs are prefetched two chunks ahead into the factor waves'
 // registers; the factors live in a double-buffered LDS area; the workgroup
 // meets at one barrier per chunk.
@@ -45,25 +48,23 @@ struct PipeCfg {
     static constexpr int NT = (NC + 2) * 64;
     static constexpr int RT = D / 16;
     static constexpr int KB = D / 32;
-    static constexpr int LDK = D + 8;  // bf16 row stride of K and V rows
-    static constexpr int LDT = 20;     // fp32 row stride of a diagonal block of N
-    static constexpr int TILE = 512;   // bf16 per pre-split 16 x 16 tile: [row][4 col groups][hi 4 | lo 4]
+    static constexpr int LDK = D + 8;   // bf16 row stride of K rows
+    static constexpr int LDV = CH + 4;  // fp32 row stride of (E V)^T
+    static constexpr int LDT = 20;      // fp32 row stride of a diagonal block of N0
+    static constexpr int TILE = 512;    // bf16 per pre-split 16 x 16 tile: [row][4 col groups][hi 4 | lo 4]
     static constexpr int al(int x) { return (x + 15) / 16 * 16; }
-    // one buffer: K rows, V rows, -N off-diagonal tiles, diagonal inverses,
-    // beta, e^Gamma, e^{Gc-Gamma}, e^Gc
+    // one buffer: K rows, (E V)^T, A_b, -M_bc, lambda
     static constexpr int bK = 0;
     static constexpr int bV = bK + al(CH * LDK * 2);
-    static constexpr int bNo = bV + al(CH * LDK * 2);
-    static constexpr int bID = bNo + 6 * TILE * 2;
-    static constexpr int bBeta = bID + 4 * TILE * 2;
-    static constexpr int bEg = bBeta + CH * 4;
-    static constexpr int bEc = bEg + CH * 4;
-    static constexpr int bLam = bEc + CH * 4;
+    static constexpr int bA = bV + al(D * LDV * 4);
+    static constexpr int bM = bA + 4 * TILE * 2;
+    static constexpr int bLam = bM + 6 * TILE * 2;
     static constexpr int BUF = al(bLam + 16);
-    // factor-wave scratch: Gamma (log2 units), diagonal blocks of N
-    static constexpr int offG = 2 * BUF;
-    static constexpr int offNt = offG + CH * 4;
-    static constexpr int total = offNt + 4 * 16 * LDT * 4;
+    // factor-wave scratch: beta, diagonal blocks of N0, their inverses (pre-split)
+    static constexpr int offB = 2 * BUF;
+    static constexpr int offN = offB + CH * 4;
+    static constexpr int offI = offN + 4 * 16 * LDT * 4;
+    static constexpr int total = offI + 4 * TILE * 2;
     static_assert(total <= 160 * 1024, "LDS budget");
 };
 
@@ -152,188 +153,182 @@ __global__ void __launch_bounds__((2 * D / 32 + 2) * 64)
 k_build_dense_pipe(BuildArgs a) {
     using Cfg = PipeCfg<D>;
     constexpr int NC = Cfg::NC, RT = Cfg::RT, KB = Cfg::KB;
-    constexpr int LDK = Cfg::LDK, LDT = Cfg::LDT, TILE = Cfg::TILE;
+    constexpr int LDK = Cfg::LDK, LDV = Cfg::LDV, LDT = Cfg::LDT, TILE = Cfg::TILE;
     constexpr float L2E = 1.4426950408889634f;
     __shared__ __attribute__((aligned(16))) char smem[Cfg::total];
-    float *sGam = reinterpret_cast<float *>(smem + Cfg::offG);
-    float *sNt = reinterpret_cast<float *>(smem + Cfg::offNt);
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform role
-    const int r16 = lane & 15, grp = lane >> 4;
     const int seg = blockIdx.x / a.n_chains, chain = blockIdx.x % a.n_chains;
     const int dk = a.dk;
     const int64_t b0 = a.seg_begin[seg], n = a.seg_end[seg] - b0;
     const int nch = (int)((n + CH - 1) / CH);
-    const bf16 *kp = reinterpret_cast<const bf16 *>(a.x.k) + (int64_t)chain * a.x.cs;
-    const bf16 *vp = reinterpret_cast<const bf16 *>(a.x.v) + (int64_t)chain * a.x.cs;
-    const bf16 *gp = FAM == GDN ? reinterpret_cast<const bf16 *>(a.x.g) + (int64_t)chain * a.x.gcs : nullptr;
-    const bf16 *bp = reinterpret_cast<const bf16 *>(a.x.beta) + (int64_t)chain * a.x.bcs;
-
-    const bool carry = wv < NC;
-    const int cbase = wv * 32;
-    const bool isS = carry && cbase >= D;
 
     // Carry waves and factor waves run separate loops that meet at the same
     // number of barriers: (nch > 0) + nch.
-    if (!carry) {
-    // the factor waves go first at issue on the SIMDs they share with carry
-    // waves: their chain of short dependent steps sets the chunk period
-    __builtin_amdgcn_s_setprio(3);
-    // prefetched token row `lane` of a chunk: D bf16 = D/8 16-byte pieces
-    constexpr int RV = D / 8;
-    bf16x8 pre[RV];
-    auto pre_put = [&](int p, const bf16x8 &v) { pre[p] = v; };
-    auto pre_get = [&](int p) { return pre[p]; };
-    bf16 gpre = (bf16)0.f, bpre = (bf16)0.f;
-    auto prefetch = [&](int c) {
-        const int64_t c0 = (int64_t)c * CH;
-        const int L = (int)(n - c0 < CH ? n - c0 : CH);
-        const int64_t t = b0 + c0 + lane;
-        const bf16 *src = (wv == NC ? kp : vp) + t * a.x.ts;
+    if (wv >= NC) {
+        // the factor waves go first at issue on the SIMDs they share with
+        // carry waves: their chains of short dependent steps set the period
+        __builtin_amdgcn_s_setprio(3);
+        const bool kw = wv == NC;  // K / factor wave, else V / gate wave
+        const int lane = tid & 63;
+        const bf16 *src = reinterpret_cast<const bf16 *>(kw ? a.x.k : a.x.v) + (int64_t)chain * a.x.cs;
+        const bf16 *gp = FAM == GDN ? reinterpret_cast<const bf16 *>(a.x.g) + (int64_t)chain * a.x.gcs : nullptr;
+        const bf16 *bp = reinterpret_cast<const bf16 *>(a.x.beta) + (int64_t)chain * a.x.bcs;
+        // token row `lane` of a chunk (D bf16 = D/8 16-byte pieces) and its
+        // beta (K wave) or gate (V wave), two chunks ahead of the carry
+        constexpr int RV = D / 8;
+        bf16x8 pre[RV];
+        bf16 spre = (bf16)0.f;
+        auto prefetch = [&](int c) {
+            const int64_t c0 = (int64_t)c * CH;
+            const int L = (int)(n - c0 < CH ? n - c0 : CH);
+            const int64_t t = b0 + c0 + lane;
+            const bf16 *row = src + t * a.x.ts;
 #pragma unroll
-        for (int p = 0; p < RV; ++p) {
-            bf16x8 v;
-            if (lane < L && 8 * p < dk) {
-                v = *reinterpret_cast<const bf16x8 *>(src + 8 * p);
-            } else {
+            for (int p = 0; p < RV; ++p) {
+                if (lane < L && 8 * p < dk) {
+                    pre[p] = *reinterpret_cast<const bf16x8 *>(row + 8 * p);
+                } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = (bf16)0.f;
-            }
-            pre_put(p, v);
-        }
-        if (wv == NC) {
-            gpre = bpre = (bf16)0.f;
-            if (lane < L) {
-                if (FAM == GDN) gpre = gp[t * a.x.gts];
-                bpre = bp[t * a.x.bts];
-            }
-        }
-    };
-    // factor-wave work for chunk c into buffer c & 1
-    auto factors = [&](int c) {
-        // lane-derived addresses are rebuilt here from an opaque copy of the
-        // lane id rather than held in registers across the chunk loop
-        int lane = tid & 63;
-        asm volatile("" : "+v"(lane));
-        const int r16 = lane & 15, grp = lane >> 4;
-        char *buf = smem + (c & 1) * Cfg::BUF;
-        bf16 *bK = reinterpret_cast<bf16 *>(buf + Cfg::bK);
-        if (wv == NC + 1) {
-            bf16 *bV = reinterpret_cast<bf16 *>(buf + Cfg::bV);
-#pragma unroll
-            for (int p = 0; p < RV; ++p) *reinterpret_cast<bf16x8 *>(bV + lane * LDK + 8 * p) = pre_get(p);
-            return;
-        }
-        bf16 *bNo = reinterpret_cast<bf16 *>(buf + Cfg::bNo);
-        bf16 *bID = reinterpret_cast<bf16 *>(buf + Cfg::bID);
-        float *bBeta = reinterpret_cast<float *>(buf + Cfg::bBeta);
-        float *bEg = reinterpret_cast<float *>(buf + Cfg::bEg);
-        float *bEc = reinterpret_cast<float *>(buf + Cfg::bEc);
-        float *bLam = reinterpret_cast<float *>(buf + Cfg::bLam);
-        // K rows; gate scan (lane = token), Gamma kept in log2 units
-#pragma unroll
-        for (int p = 0; p < RV; ++p) *reinterpret_cast<bf16x8 *>(bK + lane * LDK + 8 * p) = pre_get(p);
-        {
-            float s = 0.f, gc = 0.f;
-            if (FAM == GDN) {
-                s = wave_incl_scan((float)gpre * L2E);
-                gc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 63));
-            }
-            sGam[lane] = s;
-            bBeta[lane] = (float)bpre;
-            bEg[lane] = __builtin_amdgcn_exp2f(s);
-            bEc[lane] = __builtin_amdgcn_exp2f(gc - s);
-            if (lane == 0) bLam[0] = __builtin_amdgcn_exp2f(gc);
-        }
-        wave_lds_fence();
-        // Gram tiles, one block row b at a time.  Off-diagonal (b > c): the
-        // lane holds row t = 16b + r16, columns i = 16c + 4grp + e of -N (G is
-        // symmetric, so K_c K_b^T in C layout is that), stored pre-split.
-        // Diagonal: the lane holds rows t = 16b + 4grp + e, column i = 16b + r16,
-        // stored row-major in fp32 for the inverse below.
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            f32x4 acc[4];
-#pragma unroll
-            for (int nt = 0; nt <= mt; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const bf16x8 km = lds_cont(bK, LDK, 16 * mt + r16, 32 * kb, grp);
-#pragma unroll
-                for (int nt = 0; nt < mt; ++nt)
-                    acc[nt] = mfma(lds_cont(bK, LDK, 16 * nt + r16, 32 * kb, grp), km, acc[nt]);
-                acc[mt] = mfma(km, km, acc[mt]);
-            }
-            const float gt = sGam[16 * mt + r16], bt = bBeta[16 * mt + r16];
-#pragma unroll
-            for (int nt = 0; nt < mt; ++nt) {
-                const f32x4 gi = *reinterpret_cast<const f32x4 *>(sGam + 16 * nt + 4 * grp);
-                f32x4 v;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    v[e] = -bt * acc[nt][e];
-                    if (FAM == GDN) v[e] *= __builtin_amdgcn_exp2f(gt - gi[e]);
+                    for (int e = 0; e < 8; ++e) pre[p][e] = (bf16)0.f;
                 }
-                tile_put(bNo + (mt * (mt - 1) / 2 + nt) * TILE, r16, grp, v);
             }
-            const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sGam + 16 * mt + 4 * grp);
-            const f32x4 b4 = *reinterpret_cast<const f32x4 *>(bBeta + 16 * mt + 4 * grp);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float x = b4[e] * acc[mt][e];
-                if (FAM == GDN) x *= __builtin_amdgcn_exp2f(g4[e] - gt);
-                sNt[(16 * mt + 4 * grp + e) * LDT + r16] = (4 * grp + e > r16) ? x : 0.f;
+            spre = (bf16)0.f;
+            if (lane < L) {
+                if (kw) spre = bp[t * a.x.bts];
+                else if (FAM == GDN) spre = gp[t * a.x.gts];
             }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        wave_lds_fence();
-        // row r16 of (I + N_bb)^-1 for block b = grp: y (I + N_bb) = e_r.  Swept
-        // from the last row up: once y_i is final its multiple of row i of N_bb
-        // leaves every y_j, j < i, so the dependent chain is 16 steps long.
-        {
-            float y[16];
+        };
+        auto factors = [&](int c) {
+            // lane-derived addresses are rebuilt here from an opaque copy of
+            // the lane id rather than held in registers across the chunk loop
+            int lane = tid & 63;
+            asm volatile("" : "+v"(lane));
+            const int r16 = lane & 15, grp = lane >> 4;
+            char *buf = smem + (c & 1) * Cfg::BUF;
+            if (!kw) {
+                // gate scan (lane = token, Gamma in log2 units), lambda, (E V)^T
+                float s = 0.f, gc = 0.f;
+                if (FAM == GDN) {
+                    s = wave_incl_scan((float)spre * L2E);
+                    gc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 63));
+                }
+                const float ec = __builtin_amdgcn_exp2f(gc - s);
+                float *bV = reinterpret_cast<float *>(buf + Cfg::bV);
 #pragma unroll
-            for (int j = 0; j < 16; ++j) y[j] = (j == r16) ? 1.f : 0.f;
-            // row i of N_bb is read one step ahead of its use
-            f32x4 cur[4], nxt[4];
+                for (int p = 0; p < RV; ++p)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) cur[q] = *reinterpret_cast<const f32x4 *>(sNt + (16 * grp + 15) * LDT + 4 * q);
+                    for (int e = 0; e < 8; ++e) bV[(8 * p + e) * LDV + lane] = ec * (float)pre[p][e];
+                if (lane == 0) *reinterpret_cast<float *>(buf + Cfg::bLam) = __builtin_amdgcn_exp2f(gc);
+                return;
+            }
+            bf16 *bK = reinterpret_cast<bf16 *>(buf + Cfg::bK);
+            bf16 *bA = reinterpret_cast<bf16 *>(buf + Cfg::bA);
+            bf16 *bM = reinterpret_cast<bf16 *>(buf + Cfg::bM);
+            float *sB = reinterpret_cast<float *>(smem + Cfg::offB);
+            float *sN = reinterpret_cast<float *>(smem + Cfg::offN);
+            bf16 *sI = reinterpret_cast<bf16 *>(smem + Cfg::offI);
 #pragma unroll
-            for (int i = 15; i > 0; --i) {
+            for (int p = 0; p < RV; ++p) *reinterpret_cast<bf16x8 *>(bK + lane * LDK + 8 * p) = pre[p];
+            sB[lane] = (float)spre;
+            wave_lds_fence();
+            // Gram tiles, one block row b at a time, in C layout: the lane holds
+            // rows t = 16b + 4grp + e, column i = 16c + r16 of N0 = beta_t G_ti.
+            // Diagonal blocks go to LDS row-major for the inverse; the six
+            // off-diagonal ones stay in registers for the M products.
+            f32x4 noff[6];
 #pragma unroll
-                for (int q = 0; 4 * q < i - 1; ++q)
-                    nxt[q] = *reinterpret_cast<const f32x4 *>(sNt + (16 * grp + i - 1) * LDT + 4 * q);
+            for (int mt = 0; mt < 4; ++mt) {
+                f32x4 acc[4];
 #pragma unroll
-                for (int q = 0; 4 * q < i; ++q)
+                for (int nt = 0; nt <= mt; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (4 * q + e < i) y[4 * q + e] -= y[i] * cur[q][e];
+                for (int kb = 0; kb < KB; ++kb) {
+                    const bf16x8 km = lds_cont(bK, LDK, 16 * mt + r16, 32 * kb, grp);
+#pragma unroll
+                    for (int nt = 0; nt < mt; ++nt)
+                        acc[nt] = mfma(km, lds_cont(bK, LDK, 16 * nt + r16, 32 * kb, grp), acc[nt]);
+                    acc[mt] = mfma(km, km, acc[mt]);
+                }
+                const f32x4 b4 = *reinterpret_cast<const f32x4 *>(sB + 16 * mt + 4 * grp);
+#pragma unroll
+                for (int nt = 0; nt < mt; ++nt) noff[mt * (mt - 1) / 2 + nt] = acc[nt] * b4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sN[(16 * mt + 4 * grp + e) * LDT + r16] = (4 * grp + e > r16) ? b4[e] * acc[mt][e] : 0.f;
                 __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
             }
+            wave_lds_fence();
+            // row r16 of (I + N0_bb)^-1 for block b = grp: y (I + N0_bb) = e_r.
+            // Swept from the last row up: once y_i is final its multiple of row
+            // i of N0_bb leaves every y_j, j < i, so the dependent chain is 16
+            // steps long.  Stored pre-split as is (for M) and times diag(beta_b)
+            // (A_b).
+            {
+                float y[16];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                tile_put(bID + grp * TILE, r16, q, f32x4{y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]});
+                for (int j = 0; j < 16; ++j) y[j] = (j == r16) ? 1.f : 0.f;
+                f32x4 cur[4], nxt[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) cur[q] = *reinterpret_cast<const f32x4 *>(sN + (16 * grp + 15) * LDT + 4 * q);
+#pragma unroll
+                for (int i = 15; i > 0; --i) {
+#pragma unroll
+                    for (int q = 0; 4 * q < i - 1; ++q)
+                        nxt[q] = *reinterpret_cast<const f32x4 *>(sN + (16 * grp + i - 1) * LDT + 4 * q);
+#pragma unroll
+                    for (int q = 0; 4 * q < i; ++q)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (4 * q + e < i) y[4 * q + e] -= y[i] * cur[q][e];
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 yq = {y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]};
+                    const f32x4 bq = *reinterpret_cast<const f32x4 *>(sB + 16 * grp + 4 * q);
+                    tile_put(sI + grp * TILE, r16, q, yq);
+                    tile_put(bA + grp * TILE, r16, q, yq * bq);
+                }
+            }
+            wave_lds_fence();
+            // -M_bc: C = N0_bc^T Inv_b^T = M_bc^T in C layout, i.e. the lane
+            // holds M_bc[r16][4grp + e], the A-operand layout
+#pragma unroll
+            for (int mt = 1; mt < 4; ++mt) {
+                s4 ih, il;
+                tile_frag(sI + mt * TILE, r16, grp, ih, il);
+#pragma unroll
+                for (int nt = 0; nt < mt; ++nt) {
+                    s4 nh, nl;
+                    split4(noff[mt * (mt - 1) / 2 + nt], nh, nl);
+                    const f32x4 m = mma16(nh, nl, ih, il, f32x4{0.f, 0.f, 0.f, 0.f});
+                    tile_put(bM + (mt * (mt - 1) / 2 + nt) * TILE, r16, grp, -m);
+                }
+            }
+        };
+        if (nch > 0) {
+            prefetch(0);
+            factors(0);
+            if (nch > 1) prefetch(1);
+            __syncthreads();
         }
-    };
-    if (nch > 0) {
-        prefetch(0);
-        factors(0);
-        if (nch > 1) prefetch(1);
-        __syncthreads();
-    }
-    for (int c = 0; c < nch; ++c) {
-        if (c + 1 < nch) {
-            factors(c + 1);
-            if (c + 2 < nch) prefetch(c + 2);
+        for (int c = 0; c < nch; ++c) {
+            if (c + 1 < nch) {
+                factors(c + 1);
+                if (c + 2 < nch) prefetch(c + 2);
+            }
+            __syncthreads();
         }
-        __syncthreads();
-    }
-    return;
+        return;
     }
 
+    const int lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+    const int cbase = wv * 32;
+    const bool isS = cbase >= D;
     f32x4 X[RT][2];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -343,128 +338,106 @@ k_build_dense_pipe(BuildArgs a) {
             for (int jj = 0; jj < 4; ++jj) X[rt][nt][jj] = (16 * rt + 4 * grp + jj == cbase + 16 * nt + r16) ? 1.f : 0.f;
     if (nch > 0) __syncthreads();
     for (int c = 0; c < nch; ++c) {
-        {
-            const char *buf = smem + (c & 1) * Cfg::BUF;
-            const bf16 *bK = reinterpret_cast<const bf16 *>(buf + Cfg::bK);
-            const bf16 *bV = reinterpret_cast<const bf16 *>(buf + Cfg::bV);
-            const bf16 *bNo = reinterpret_cast<const bf16 *>(buf + Cfg::bNo);
-            const bf16 *bID = reinterpret_cast<const bf16 *>(buf + Cfg::bID);
-            const float *bBeta = reinterpret_cast<const float *>(buf + Cfg::bBeta);
-            const float *bEg = reinterpret_cast<const float *>(buf + Cfg::bEg);
-            const float *bEc = reinterpret_cast<const float *>(buf + Cfg::bEc);
-            const float lam = *reinterpret_cast<const float *>(buf + Cfg::bLam);
-            // Z = K X
-            f32x4 Z[4][2];
+        const char *buf = smem + (c & 1) * Cfg::BUF;
+        const bf16 *bK = reinterpret_cast<const bf16 *>(buf + Cfg::bK);
+        const float *bV = reinterpret_cast<const float *>(buf + Cfg::bV);
+        const bf16 *bA = reinterpret_cast<const bf16 *>(buf + Cfg::bA);
+        const bf16 *bM = reinterpret_cast<const bf16 *>(buf + Cfg::bM);
+        const float lam = FAM == GDN ? *reinterpret_cast<const float *>(buf + Cfg::bLam) : 1.f;
+        // Z = K X
+        f32x4 Z[4][2];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) Z[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int nt = 0; nt < 2; ++nt) Z[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                bf16x8 xh[2], xl[2];
+        for (int kb = 0; kb < KB; ++kb) {
+            bf16x8 xh[2], xl[2];
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    float xv[8];
-                    acc_to_perm(X[2 * kb][nt], X[2 * kb + 1][nt], xv);
-                    split8(xv, xh[nt], xl[nt]);
-                }
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    const bf16x8 kh = lds_perm(bK, LDK, 16 * mt + r16, 32 * kb, grp);
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        Z[mt][nt] = mfma(kh, xh[nt], Z[mt][nt]);
-                        Z[mt][nt] = mfma(kh, xl[nt], Z[mt][nt]);
-                    }
-                }
+            for (int nt = 0; nt < 2; ++nt) {
+                float xv[8];
+                acc_to_perm(X[2 * kb][nt], X[2 * kb + 1][nt], xv);
+                split8(xv, xh[nt], xl[nt]);
             }
-            // diag(beta) Y = diag(beta) ([0 | V] - diag(e^Gamma) Z), in Z
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                const f32x4 eg = *reinterpret_cast<const f32x4 *>(bEg + 16 * mt + 4 * grp);
-                const f32x4 bt = *reinterpret_cast<const f32x4 *>(bBeta + 16 * mt + 4 * grp);
+                const bf16x8 kh = lds_perm(bK, LDK, 16 * mt + r16, 32 * kb, grp);
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) Z[mt][nt][jj] = -Z[mt][nt][jj] * eg[jj];
-                    if (isS) {
-                        const bf16x4 v4 = lds_tr4(bV, LDK, 16 * mt + 4 * grp, cbase - D + 16 * nt, r16);
-#pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) Z[mt][nt][jj] += (float)v4[jj];
-                    }
-                    Z[mt][nt] *= bt;
+                    Z[mt][nt] = mfma(kh, xh[nt], Z[mt][nt]);
+                    Z[mt][nt] = mfma(kh, xl[nt], Z[mt][nt]);
                 }
             }
-            // R_b = (I + N_bb)^-1 (diag(beta) Y_b - sum_{c<b} N_bc R_c), R_b replacing Y_b;
-            // the split R blocks are kept for the blocks below them
-            s4 Rh[3][2], Rl[3][2];
+        }
+        // Y = [0 | E V] - lambda Z, split
+        s4 Yh[4][2], Yl[4][2];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int c2 = 0; c2 < b; ++c2) {
-                    s4 nh, nl;
-                    tile_frag(bNo + (b * (b - 1) / 2 + c2) * TILE, r16, grp, nh, nl);
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) Z[b][nt] = mma16(nh, nl, Rh[c2][nt], Rl[c2][nt], Z[b][nt]);
-                }
-                s4 ih, il;
-                tile_frag(bID + b * TILE, r16, grp, ih, il);
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    s4 yh, yl;
-                    split4(Z[b][nt], yh, yl);
-                    Z[b][nt] = mma16(ih, il, yh, yl, f32x4{0.f, 0.f, 0.f, 0.f});
-                    if (b < 3) split4(Z[b][nt], Rh[b][nt], Rl[b][nt]);
-                }
+            for (int nt = 0; nt < 2; ++nt) {
+                f32x4 y = -lam * Z[mt][nt];
+                if (isS) y += *reinterpret_cast<const f32x4 *>(bV + (cbase - D + 16 * nt + r16) * LDV + 16 * mt + 4 * grp);
+                split4(y, Yh[mt][nt], Yl[mt][nt]);
             }
-            // X = e^{Gamma_c} X + K^T diag(e^{Gamma_c - Gamma}) R
+        // R'_b = A_b Y_b - sum_{c<b} M_bc R'_c, kept split
+        s4 Rh[4][2], Rl[4][2];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            f32x4 r[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            s4 ah, al;
+            tile_frag(bA + b * TILE, r16, grp, ah, al);
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) r[nt] = mma16(ah, al, Yh[b][nt], Yl[b][nt], r[nt]);
+#pragma unroll
+            for (int c2 = 0; c2 < b; ++c2) {
+                s4 mh, ml;
+                tile_frag(bM + (b * (b - 1) / 2 + c2) * TILE, r16, grp, mh, ml);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) r[nt] = mma16(mh, ml, Rh[c2][nt], Rl[c2][nt], r[nt]);
+            }
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) split4(r[nt], Rh[b][nt], Rl[b][nt]);
+        }
+        // X = lambda X + K^T R'
+        if (FAM == GDN) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) X[rt][nt] *= lam;
+        }
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const f32x4 ec = *reinterpret_cast<const f32x4 *>(bEc + 16 * mt + 4 * grp);
+        for (int h = 0; h < 2; ++h) {
+            bf16x8 rh[2], rl[2];
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) Z[mt][nt] *= ec;
+            for (int nt = 0; nt < 2; ++nt) {
+                rh[nt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(Rh[2 * h][nt], Rh[2 * h + 1][nt], 0, 1, 2, 3, 4, 5, 6, 7));
+                rl[nt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(Rl[2 * h][nt], Rl[2 * h + 1][nt], 0, 1, 2, 3, 4, 5, 6, 7));
             }
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                bf16x8 rh[2], rl[2];
+            for (int rt = 0; rt < RT; ++rt) {
+                const bf16x8 kt = lds_tr_perm(bK, LDK, 32 * h, 16 * rt, r16, grp);
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
-                    float rv[8];
-                    acc_to_perm(Z[2 * h][nt], Z[2 * h + 1][nt], rv);
-                    split8(rv, rh[nt], rl[nt]);
-                }
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    const bf16x8 kt = lds_tr_perm(bK, LDK, 32 * h, 16 * rt, r16, grp);
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        X[rt][nt] = mfma(kt, rh[nt], X[rt][nt]);
-                        X[rt][nt] = mfma(kt, rl[nt], X[rt][nt]);
-                    }
+                    X[rt][nt] = mfma(kt, rh[nt], X[rt][nt]);
+                    X[rt][nt] = mfma(kt, rl[nt], X[rt][nt]);
                 }
             }
         }
         __syncthreads();
     }
 
-    {
-        float *To = a.T + ((int64_t)seg * a.n_chains + chain) * dk * dk;
-        float *So = a.S + ((int64_t)seg * a.n_chains + chain) * dk * dk;
+    float *To = a.T + ((int64_t)seg * a.n_chains + chain) * dk * dk;
+    float *So = a.S + ((int64_t)seg * a.n_chains + chain) * dk * dk;
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int row = 16 * rt + 4 * grp + jj;
-                    const int col = cbase + 16 * nt + r16 - (isS ? D : 0);
-                    if (row < dk && col < dk) (isS ? So : To)[row * dk + col] = X[rt][nt][jj];
-                }
-    }
+            for (int jj = 0; jj < 4; ++jj) {
+                const int row = 16 * rt + 4 * grp + jj;
+                const int col = cbase + 16 * nt + r16 - (isS ? D : 0);
+                if (row < dk && col < dk) (isS ? So : To)[row * dk + col] = X[rt][nt][jj];
+            }
 }
 
 template <int D, int FAM>

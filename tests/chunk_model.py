@@ -84,3 +84,39 @@ def chunk_run(fam, q, k, v, g=None, beta=None, gamma=1.0, S0=None, c=64):
             O[s + t] = o
         S = np.exp(Gm[-1])[:, None] * S + Kt.T @ X
     return S, O
+
+
+def chunk_pair_folded(fam, k, v, g=None, beta=None, c=64, blk=16):
+    """The dense-build form with the scalar decay folded out of the chunk
+    system (DeltaNet, Gated DeltaNet).  With E = diag(exp(Gam_c - Gam_t)) the
+    decayed system is a similarity transform of the undecayed one,
+    I + diag(beta) tril(G o exp(Gam_t - Gam_i), -1) = E^-1 (I + N0) E with
+    N0 = diag(beta) tril(K K^T, -1), so R' = E R solves
+        (I + N0) R' = diag(beta) ([0 | E V] - exp(Gam_c) K X)
+    and X <- exp(Gam_c) X + K^T R'.  R' is found block by block:
+        R'_b = Inv_b diag(beta_b) Y'_b - sum_{c<b} Inv_b N0_bc R'_c,
+    Inv_b = (I + N0_bb)^-1, which is how the bf16 kernel splits the work."""
+    k, v = np.asarray(k, np.float64), np.asarray(v, np.float64)
+    n, dk = k.shape
+    dv = v.shape[1]
+    lg = np.zeros(n) if fam == "deltanet" else np.asarray(g, np.float64).reshape(n)
+    bb = np.asarray(beta, np.float64)
+    X = np.concatenate([np.eye(dk), np.zeros((dk, dv))], axis=1)
+    for s in range(0, n, c):
+        e = min(n, s + c)
+        L = e - s
+        K, V, b = k[s:e], v[s:e], bb[s:e]
+        Gm = np.cumsum(lg[s:e])
+        lam = np.exp(Gm[-1])
+        ec = np.exp(Gm[-1] - Gm)
+        N0 = np.diag(b) @ np.tril(K @ K.T, -1)
+        Y = np.concatenate([np.zeros((L, dk)), ec[:, None] * V], axis=1) - lam * (K @ X)
+        R = np.zeros_like(Y)
+        for b0 in range(0, L, blk):
+            b1 = min(L, b0 + blk)
+            inv = np.linalg.inv(np.eye(b1 - b0) + N0[b0:b1, b0:b1])
+            acc = inv @ np.diag(b[b0:b1]) @ Y[b0:b1]
+            acc -= inv @ N0[b0:b1, :b0] @ R[:b0]
+            R[b0:b1] = acc
+        X = lam * X + K.T @ R
+    return X[:, :dk], X[:, dk:]

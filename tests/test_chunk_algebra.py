@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 import oracle
-from chunk_model import chunk_pair, chunk_run
+from chunk_model import chunk_pair, chunk_pair_folded, chunk_run
 
 FAMS = ["linear", "retnet", "mamba2", "gla", "deltanet", "gdn", "kda"]
 
@@ -44,3 +44,19 @@ def test_chunk_outputs_match_oracle(fam, c):
     Sc, Oc = chunk_run(fam, q, k, v, g, beta, gamma, S0, c)
     assert oracle.rel_fro(Sc, S) < 1e-11
     assert oracle.rel_fro(Oc, O) < 1e-11
+
+
+@pytest.mark.parametrize("fam", ["deltanet", "gdn"])
+@pytest.mark.parametrize("law", ["moderate", "strong"])
+def test_folded_decay_form_matches_oracle(fam, law):
+    """The decay-folded block solve of the bf16 dense build equals the oracle,
+    also under gates strong enough that exp(Gam_c) underflows fp32."""
+    rng = np.random.default_rng(130 + (fam == "gdn") * 2 + (law == "strong"))
+    for n in (1, 17, 64, 65, 150):
+        q, k, v, g, beta, gamma = _inputs(rng, fam, n, 8, 6)
+        if fam == "gdn" and law == "strong":
+            g = -np.log1p(np.exp(rng.normal(1.5, 0.5, size=n)))
+        T, S = oracle.pair(fam, k, v, g, beta, gamma)
+        Tc, Sc = chunk_pair_folded(fam, k, v, g, beta)
+        assert oracle.rel_fro(Tc, T) < 1e-11 or np.linalg.norm(T) < 1e-200, (n, law)
+        assert oracle.rel_fro(Sc, S) < 1e-11, (n, law)
