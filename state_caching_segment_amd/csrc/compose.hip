@@ -10,10 +10,11 @@
 //
 // Sequential mode: one workgroup per (request, chain) with d/32 waves; wave w
 // keeps columns 32w .. 32w+31 of the running state in MFMA accumulators for
-// the whole list.  Dense T: S <- T S + S_slot as a small GEMM on the matrix
-// cores, T streamed from HBM straight into A operands and the state fed back
-// as the B operand (three-pass bf16 split for bf16 inputs, fp32 matrix cores
-// for fp32 inputs; fp32 state either way).  Diagonal T: a row scale plus add.
+// the whole list.  Dense T (k_compose_dense): S <- T S + S_slot as a small GEMM
+// on the matrix cores, T staged once per workgroup through LDS one entry ahead
+// and the state fed back as the B operand (three-pass bf16 split for bf16
+// inputs, fp32 matrix cores for fp32 inputs; fp32 state either way).
+// Diagonal T (k_compose_seq): a row scale plus add.
 // The seam recurrence runs on the vector ALUs over the same registers.
 //
 // Tree mode, the associative form (T_b, S_b) o (T_a, S_a) = (T_b T_a,
@@ -37,7 +38,7 @@ template <int D, int FAM, typename TIN>
 __global__ void __launch_bounds__(D / 32 * 64)
 k_compose_seq(ComposeArgs a) {
     constexpr bool F32 = std::is_same<TIN, float>::value;
-    __shared__ SeamSmem<D> sm;
+    __shared__ SeamSmem<D, FAM> sm;
     const int wv = threadIdx.x >> 6;
     const int req = blockIdx.x / a.n_chains, chain = blockIdx.x % a.n_chains;
     const int dk = a.dk, c0 = wv * 32;
@@ -74,7 +75,7 @@ k_compose_seq(ComposeArgs a) {
 template <int D, int FAM, typename TIN>
 __global__ void __launch_bounds__(D / 32 * 64)
 k_seam_advance(SeamArgs a) {
-    __shared__ SeamSmem<D> sm;
+    __shared__ SeamSmem<D, FAM> sm;
     const int wv = threadIdx.x >> 6;
     const int item = blockIdx.x / a.n_chains, chain = blockIdx.x % a.n_chains;
     const int dk = a.dk, c0 = wv * 32;
@@ -93,6 +94,228 @@ k_seam_advance(SeamArgs a) {
     store_tile<D>(X, st, dk, dk, c0, dk);
 }
 
+// Sequential compose for dense T (DeltaNet, GDN, KDA).  The workgroup owns one
+// (request, chain); wave w keeps columns 32w .. 32w+31 of the running state in
+// MFMA accumulators.  Each entry's T is read from HBM once per workgroup: every
+// wave loads its share of T's rows one entry ahead into registers and, once
+// the previous product is done, writes them into the LDS copy of T -- split
+// into hi and lo bf16 halves of each row for bf16 inputs (fp32 rows for fp32
+// inputs) -- from which all waves take their A operands.  The LDS copy is
+// double-buffered, so T_{j+1} is written while T_j is in use and T_{j+2} is
+// in flight.  The entry's S columns of each wave are requested as soon as the
+// previous ones have seeded the accumulators of S <- T S + S_j, so their loads
+// overlap the product.
+template <int D, bool F32>
+struct DenseTLds {
+    static constexpr int LDT = F32 ? D + 4 : 2 * D + 8;  // elements per T row: fp32, or [hi | lo] bf16
+    static constexpr int BYTES = D * LDT * (F32 ? 4 : 2);
+};
+
+template <int D, int FAM, typename TIN>
+__global__ void __launch_bounds__(D / 32 * 64)
+k_compose_dense(ComposeArgs a) {
+    constexpr bool F32 = std::is_same<TIN, float>::value;
+    constexpr int NW = D / 32, RT = D / 16, KB = D / 32;
+    using TL = DenseTLds<D, F32>;
+    constexpr int LDT = TL::LDT;
+    constexpr int NV = D * D / 4 / 64 / NW;  // 16-byte pieces of T per lane
+    constexpr int RPW = D / NW;              // T rows staged by one wave
+    __shared__ __attribute__((aligned(16))) char tsm[2][TL::BYTES];
+    __shared__ SeamSmem<D, FAM> sm;
+    constexpr bool CHUNK_SEAM = !F32 && (FAM == DELTANET || FAM == GDN);
+    __shared__ float seam_nm[CHUNK_SEAM ? NW : 1][2][SEAM_STAGE][9];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int r16 = lane & 15, grp = lane >> 4;
+    const int req = blockIdx.x / a.n_chains, chain = blockIdx.x % a.n_chains;
+    // d = 64 and d = 128 run unpadded (dk == D), which makes every offset below
+    // a compile-time constant off one per-lane base
+    const int dk = D >= 64 ? D : a.dk, c0 = wv * 32;
+    float *st = a.state + ((int64_t)req * a.n_chains + chain) * dk * dk;
+    const int e0 = a.list_off[req], m = a.list_off[req + 1] - e0;
+
+    // pair ids and seam starts of 64 entries at a time: lane l holds entry
+    // base + l, read back with readlane (no dependent scalar loads per entry)
+    int win_base = 0, win_pid = 0;
+    int64_t win_sb = -1;
+    auto win_load = [&](int b) {
+        win_base = b;
+        const int idx = b + lane < m ? b + lane : m - 1;
+        win_pid = a.pair_id[e0 + idx];
+        win_sb = a.has_seam ? a.seam_begin[e0 + idx] : -1;
+    };
+    auto pid_at = [&](int j) -> int64_t { return __builtin_amdgcn_readlane(win_pid, j - win_base); };
+    auto sb_at = [&](int j) -> int64_t {
+        const uint64_t u = (uint64_t)win_sb;
+        const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, j - win_base);
+        const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), j - win_base);
+        return (int64_t)(((uint64_t)hi << 32) | lo);
+    };
+
+    f32x4 tpre[NV];
+    f32x4 spre[RT][2];  // S_j rows: lane (4q + i, grp) holds row 4 grp + i, columns 4q .. 4q+3 of each tile
+    auto t_load = [&](int j) {
+        const float *Tp = a.T + (pid_at(j) * a.n_chains + chain) * a.t_elems;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int item = i * 64 + lane, row = wv * RPW + item / (D / 4), c4 = item % (D / 4);
+            if (D >= 64) {
+                tpre[i] = *reinterpret_cast<const f32x4 *>(Tp + row * D + 4 * c4);
+            } else {
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(Tp + (row < dk ? row : dk - 1) * dk +
+                                                                 (4 * c4 < dk ? 4 * c4 : dk - 4));
+                tpre[i] = (row < dk && 4 * c4 < dk) ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    };
+    auto t_put = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int item = i * 64 + lane, row = wv * RPW + item / (D / 4), c4 = item % (D / 4);
+            if (F32) {
+                *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(tsm[buf]) + row * LDT + 4 * c4) = tpre[i];
+            } else {
+                // columns permuted within each 32-block so that a lane's A
+                // fragment (k = 4grp.., 16+4grp..) is 8 consecutive bf16
+                const int sub = c4 % 8, pos = 32 * (c4 / 8) + 8 * (sub % 4) + 4 * (sub / 4);
+                bf16x4 h, l;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    h[e] = (bf16)tpre[i][e];
+                    l[e] = (bf16)(tpre[i][e] - (float)h[e]);
+                }
+                bf16 *tr = reinterpret_cast<bf16 *>(tsm[buf]) + row * LDT;
+                *reinterpret_cast<bf16x4 *>(tr + pos) = h;
+                *reinterpret_cast<bf16x4 *>(tr + D + pos) = l;
+            }
+        }
+    };
+    auto s_load = [&](int j) {
+        const float *Sp = a.S + (pid_at(j) * a.n_chains + chain) * dk * dk;
+        const int rw = 4 * grp + (r16 & 3), cl = c0 + 4 * (r16 >> 2);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const int row = 16 * rt + rw, col = cl + 16 * nt;
+                if (D >= 64) {
+                    spre[rt][nt] = *reinterpret_cast<const f32x4 *>(Sp + row * D + col);
+                } else {
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(Sp + (row < dk ? row : dk - 1) * dk +
+                                                                     (col < dk ? col : dk - 4));
+                    spre[rt][nt] = (row < dk && col < dk) ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+    };
+    // seam tokens of the next entry, fetched ahead when the whole window fits
+    // one staging stage and the gate is a scalar per token
+    SeamPrefetch<D, TIN> seam_pf;
+    const bool seam_one_stage = !fam_vgate(FAM) && a.has_seam && a.w <= SEAM_STAGE;
+
+    f32x4 X[RT][2];
+    load_tile<D>(X, st, dk, dk, c0, dk);
+    if (m > 0) {
+        win_load(0);
+        t_load(0);
+        s_load(0);
+        t_put(0);
+        if (m > 1) t_load(1);
+        if (seam_one_stage && sb_at(0) >= 0) seam_fetch<D, FAM, TIN>(seam_pf, a.x, chain, dk, sb_at(0), a.w);
+        __syncthreads();
+    }
+    for (int j = 0; j < m; ++j) {
+        const int e = e0 + j;
+        if (j + 2 >= win_base + 64) win_load(j);
+        if (a.has_seam) {
+            const int64_t sb = sb_at(j);
+            if (sb >= 0) {
+                for (int s0 = 0; s0 < a.w; s0 += SEAM_STAGE) {
+                    const int nt = a.w - s0 < SEAM_STAGE ? a.w - s0 : SEAM_STAGE;
+                    __syncthreads();
+                    if (seam_one_stage)
+                        seam_put<D, FAM, TIN>(sm, seam_pf, dk, nt);
+                    else
+                        stage_seam<D, FAM, TIN>(sm, a.x, chain, dk, sb + s0, nt);
+                    __syncthreads();
+                    float *o_first = a.o + (((int64_t)e * a.w + s0) * a.n_chains + chain) * dk;
+                    if constexpr (CHUNK_SEAM)
+                        seam_chunk_bf16<D, FAM>(X, sm, nt, o_first, (int64_t)a.n_chains * dk, c0, dk,
+                                                seam_nm[wv][0], seam_nm[wv][1]);
+                    else
+                        seam_tokens<D, FAM>(X, sm, nt, o_first, (int64_t)a.n_chains * dk, c0, c0, false, dk);
+                }
+            }
+        }
+        // S <- T_j S + S_j; the next S_j is requested as soon as this one is in
+        // the accumulators
+        if (F32) {
+            float xv[KB][2][8];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) acc_to_perm(X[2 * kb][nt], X[2 * kb + 1][nt], xv[kb][nt]);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) X[rt][nt] = quad_transpose(spre[rt][nt], lane);
+            if (j + 1 < m) {
+                s_load(j + 1);
+                if (seam_one_stage && sb_at(j + 1) >= 0)
+                    seam_fetch<D, FAM, TIN>(seam_pf, a.x, chain, dk, sb_at(j + 1), a.w);
+            }
+            const float *tf = reinterpret_cast<const float *>(tsm[j & 1]);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    float tv[8];
+                    lds_perm_f(tf, LDT, 16 * rt + r16, 32 * kb, grp, tv);
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) X[rt][nt] = mma_f32(tv, xv[kb][nt], X[rt][nt]);
+                }
+        } else {
+            bf16x8 xh[KB][2], xl[KB][2];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    float xv[8];
+                    acc_to_perm(X[2 * kb][nt], X[2 * kb + 1][nt], xv);
+                    split8(xv, xh[kb][nt], xl[kb][nt]);
+                }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) X[rt][nt] = quad_transpose(spre[rt][nt], lane);
+            if (j + 1 < m) {
+                s_load(j + 1);
+                if (seam_one_stage && sb_at(j + 1) >= 0)
+                    seam_fetch<D, FAM, TIN>(seam_pf, a.x, chain, dk, sb_at(j + 1), a.w);
+            }
+            const bf16 *th = reinterpret_cast<const bf16 *>(tsm[j & 1]);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const int off = (16 * rt + r16) * LDT + 32 * kb + 8 * grp;
+                    const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(th + off);
+                    const bf16x8 al = *reinterpret_cast<const bf16x8 *>(th + D + off);
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        X[rt][nt] = mfma(ah, xh[kb][nt], X[rt][nt]);
+                        X[rt][nt] = mfma(ah, xl[kb][nt], X[rt][nt]);
+                        X[rt][nt] = mfma(al, xh[kb][nt], X[rt][nt]);
+                    }
+                }
+        }
+        if (j + 1 < m) {
+            t_put((j + 1) & 1);  // that buffer's last readers finished entry j - 1
+            if (j + 2 < m) t_load(j + 2);
+        }
+        __syncthreads();
+    }
+    store_tile<D>(X, st, dk, dk, c0, dk);
+}
+
 // ---- tree mode --------------------------------------------------------------
 
 // phase 1: block aggregates, block-local seam outputs and pulled-back queries
@@ -101,7 +324,7 @@ __global__ void __launch_bounds__(2 * D / 32 * 64)
 k_tree_block(TreeArgs t) {
     constexpr bool F32 = std::is_same<TIN, float>::value;
     const ComposeArgs &a = t.c;
-    __shared__ SeamSmem<D> sm;
+    __shared__ SeamSmem<D, FAM> sm;
     const int wv = threadIdx.x >> 6;
     const int chain = blockIdx.x % a.n_chains;
     const int rb = blockIdx.x / a.n_chains, req = rb / t.NB, blk = rb % t.NB;
@@ -241,8 +464,11 @@ k_tree_fix(TreeArgs t) {
 
 template <int D, int FAM, typename TIN>
 static hipError_t launch_compose(const ComposeArgs &a, int n_req, hipStream_t st) {
-    hipLaunchKernelGGL((k_compose_seq<D, FAM, TIN>), dim3((unsigned)(n_req * (int64_t)a.n_chains)), dim3(D / 32 * 64), 0,
-                       st, a);
+    const dim3 grid((unsigned)(n_req * (int64_t)a.n_chains)), block(D / 32 * 64);
+    if constexpr (fam_dense(FAM))
+        hipLaunchKernelGGL((k_compose_dense<D, FAM, TIN>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((k_compose_seq<D, FAM, TIN>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 

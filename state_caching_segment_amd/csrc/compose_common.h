@@ -15,49 +15,49 @@ namespace hy {
 constexpr int SEAM_STAGE = 8;  // seam tokens staged in LDS at a time
 
 // Up to SEAM_STAGE seam tokens of one chain, fp32; decays already exponentiated.
-template <int D>
+// a[t][i]: per-row decay (GLA, KDA); a[t][0]: scalar decay (other families).
+template <int D, int FAM>
 struct SeamSmem {
     float q[SEAM_STAGE][D];
     float k[SEAM_STAGE][D];
     float v[SEAM_STAGE][D];
-    float a[SEAM_STAGE][D];  // per-row decay (GLA, KDA), or a[t][0] (scalar decay)
+    float a[SEAM_STAGE][fam_vgate(FAM) ? D : 1];
     float beta[SEAM_STAGE];
 };
 
 // Stage tokens tok0 .. tok0+nt-1 of `chain` (rows past nt are zero tokens).
 template <int D, int FAM, typename TIN>
-__device__ void stage_seam(SeamSmem<D> &sm, const Tok &x, int chain, int dk, int64_t tok0, int nt) {
+__device__ void stage_seam(SeamSmem<D, FAM> &sm, const Tok &x, int chain, int dk, int64_t tok0, int nt) {
     const int tid = threadIdx.x, nthr = blockDim.x;
     const TIN *qp = reinterpret_cast<const TIN *>(x.q) + (int64_t)chain * x.cs;
     const TIN *kp = reinterpret_cast<const TIN *>(x.k) + (int64_t)chain * x.cs;
     const TIN *vp = reinterpret_cast<const TIN *>(x.v) + (int64_t)chain * x.cs;
+    // loads are unconditional, from indices clamped into the valid range, and
+    // masked afterwards: a load under a branch would make every one of them
+    // wait for its data before the branch closes
     for (int item = tid; item < SEAM_STAGE * D; item += nthr) {
         const int t = item / D, i = item % D;
-        float qv = 0.f, kv = 0.f, vv = 0.f, av = 1.f;
-        if (t < nt && i < dk) {
-            const int64_t off = (tok0 + t) * x.ts + i;
-            qv = ldf(qp + off);
-            kv = ldf(kp + off);
-            vv = ldf(vp + off);
-            if (fam_vgate(FAM))
-                av = expf(ldf(reinterpret_cast<const TIN *>(x.g) + (int64_t)chain * x.gcs + (tok0 + t) * x.gts + i));
+        const bool ok = t < nt && i < dk;
+        const int64_t off = (tok0 + (t < nt ? t : nt - 1)) * x.ts + (i < dk ? i : dk - 1);
+        const float qv = ldf(qp + off), kv = ldf(kp + off), vv = ldf(vp + off);
+        sm.q[t][i] = ok ? qv : 0.f;
+        sm.k[t][i] = ok ? kv : 0.f;
+        sm.v[t][i] = ok ? vv : 0.f;
+        if (fam_vgate(FAM)) {
+            const float gv = ldf(reinterpret_cast<const TIN *>(x.g) + (int64_t)chain * x.gcs +
+                                 (tok0 + (t < nt ? t : nt - 1)) * x.gts + (i < dk ? i : dk - 1));
+            sm.a[t][i] = ok ? expf(gv) : 1.f;
         }
-        sm.q[t][i] = qv;
-        sm.k[t][i] = kv;
-        sm.v[t][i] = vv;
-        if (fam_vgate(FAM)) sm.a[t][i] = av;
     }
     if (tid < SEAM_STAGE) {
         const int t = tid;
+        const int64_t tc = tok0 + (t < nt ? t : nt - 1);
         float av = 1.f, bv = 1.f;
-        if (t < nt) {
-            if (fam_sgate(FAM))
-                av = expf(ldf(reinterpret_cast<const TIN *>(x.g) + (int64_t)chain * x.gcs + (tok0 + t) * x.gts));
-            if (FAM == RETNET) av = x.gamma[chain];
-            if (fam_beta(FAM)) bv = ldf(reinterpret_cast<const TIN *>(x.beta) + (int64_t)chain * x.bcs + (tok0 + t) * x.bts);
-        }
-        if (!fam_vgate(FAM)) sm.a[t][0] = av;
-        sm.beta[t] = bv;
+        if (fam_sgate(FAM)) av = expf(ldf(reinterpret_cast<const TIN *>(x.g) + (int64_t)chain * x.gcs + tc * x.gts));
+        if (FAM == RETNET) av = x.gamma[chain];
+        if (fam_beta(FAM)) bv = ldf(reinterpret_cast<const TIN *>(x.beta) + (int64_t)chain * x.bcs + tc * x.bts);
+        if (!fam_vgate(FAM)) sm.a[t][0] = t < nt ? av : 1.f;
+        sm.beta[t] = t < nt ? bv : 1.f;
     }
 }
 
@@ -67,7 +67,7 @@ __device__ void stage_seam(SeamSmem<D> &sm, const Tok &x, int chain, int dk, int
 // vcol: the tile's first column in v; v_zero: the tile's v is zero (the T half
 // of a [T | S] pair, which then yields T^T q, the pulled-back query).
 template <int D, int FAM>
-__device__ void seam_tokens(f32x4 (&X)[D / 16][2], const SeamSmem<D> &sm, int nt, float *o_first,
+__device__ void seam_tokens(f32x4 (&X)[D / 16][2], const SeamSmem<D, FAM> &sm, int nt, float *o_first,
                             int64_t o_tok_stride, int ocol, int vcol, bool v_zero, int ncols) {
     constexpr int RT = D / 16;
     const int lane = lane_id(), r16 = lane & 15, grp = lane >> 4;
@@ -139,7 +139,255 @@ __device__ void seam_tokens(f32x4 (&X)[D / 16][2], const SeamSmem<D> &sm, int nt
     }
 }
 
-// Tile <- p[row * ld + c0 + c] (rows < nrows, columns c0 + c < ncols), zero elsewhere.
+// Lane i of each quad of lanes holds row i of a 4 x 4 block (4 fp32); after
+// the exchange it holds column i (DPP quad permutations: swap neighbours, then
+// swap pairs).
+template <int CTRL>
+__device__ __forceinline__ float quad_move(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 r, int lane) {
+    const bool odd = lane & 1, hi = lane & 2;
+    float t = quad_move<0xB1>(odd ? r[0] : r[1]);  // quad_perm [1,0,3,2]
+    if (odd) r[0] = t; else r[1] = t;
+    t = quad_move<0xB1>(odd ? r[2] : r[3]);
+    if (odd) r[2] = t; else r[3] = t;
+    const float t0 = quad_move<0x4E>(hi ? r[0] : r[2]);  // quad_perm [2,3,0,1]
+    const float t1 = quad_move<0x4E>(hi ? r[1] : r[3]);
+    if (hi) {
+        r[0] = t0;
+        r[1] = t1;
+    } else {
+        r[2] = t0;
+        r[3] = t1;
+    }
+    return r;
+}
+
+// One seam stage's tokens, fetched into registers ahead of use: thread tid
+// covers token tid / (D/4), features 4 (tid % (D/4)) .. +3 of q, k and v, and
+// (for the first feature quad) the token's gate and beta.
+template <int D, typename TIN>
+struct SeamPrefetch {
+    using V4 = typename std::conditional<std::is_same<TIN, float>::value, f32x4, bf16x4>::type;
+    V4 q, k, v;
+    TIN g, b;
+};
+
+template <int D, int FAM, typename TIN>
+__device__ __forceinline__ void seam_fetch(SeamPrefetch<D, TIN> &p, const Tok &x, int chain, int dk, int64_t tok0, int nt) {
+    using V4 = typename SeamPrefetch<D, TIN>::V4;
+    const int tid = threadIdx.x, t = tid / (D / 4), i = 4 * (tid % (D / 4));
+    const int64_t tc = tok0 + (t < nt ? t : nt - 1);
+    const int64_t off = (int64_t)chain * x.cs + tc * x.ts + (i < dk ? i : dk - 4);
+    p.q = *reinterpret_cast<const V4 *>(reinterpret_cast<const TIN *>(x.q) + off);
+    p.k = *reinterpret_cast<const V4 *>(reinterpret_cast<const TIN *>(x.k) + off);
+    p.v = *reinterpret_cast<const V4 *>(reinterpret_cast<const TIN *>(x.v) + off);
+    if (fam_sgate(FAM)) p.g = reinterpret_cast<const TIN *>(x.g)[(int64_t)chain * x.gcs + tc * x.gts];
+    if (fam_beta(FAM)) p.b = reinterpret_cast<const TIN *>(x.beta)[(int64_t)chain * x.bcs + tc * x.bts];
+}
+
+// Write a fetched stage into the LDS staging area (zero tokens past nt).
+template <int D, int FAM, typename TIN>
+__device__ __forceinline__ void seam_put(SeamSmem<D, FAM> &sm, const SeamPrefetch<D, TIN> &p, int dk, int nt) {
+    const int tid = threadIdx.x, t = tid / (D / 4), i = 4 * (tid % (D / 4));
+    const bool ok = t < nt && i < dk;
+    f32x4 q4, k4, v4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        q4[e] = ok ? (float)p.q[e] : 0.f;
+        k4[e] = ok ? (float)p.k[e] : 0.f;
+        v4[e] = ok ? (float)p.v[e] : 0.f;
+    }
+    *reinterpret_cast<f32x4 *>(&sm.q[t][i]) = q4;
+    *reinterpret_cast<f32x4 *>(&sm.k[t][i]) = k4;
+    *reinterpret_cast<f32x4 *>(&sm.v[t][i]) = v4;
+    if (i == 0) {
+        sm.a[t][0] = (fam_sgate(FAM) && t < nt) ? expf((float)p.g) : 1.f;
+        sm.beta[t] = (fam_beta(FAM) && t < nt) ? (float)p.b : 1.f;
+    }
+}
+
+typedef short s4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ s4v bf4(float a, float b, float c, float d) {
+    return s4v{__builtin_bit_cast(short, (bf16)a), __builtin_bit_cast(short, (bf16)b), __builtin_bit_cast(short, (bf16)c),
+               __builtin_bit_cast(short, (bf16)d)};
+}
+
+__device__ __forceinline__ void split4v(const f32x4 &x, s4v &h, s4v &l) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bf16 y = (bf16)x[e];
+        h[e] = __builtin_bit_cast(short, y);
+        l[e] = __builtin_bit_cast(short, (bf16)(x[e] - (float)y));
+    }
+}
+
+__device__ __forceinline__ f32x4 mfma16(const s4v &a, const s4v &b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Up to SEAM_STAGE seam tokens of a scalar-gate erasing family (DeltaNet,
+// GDN) with bf16-exact staged q, k, v, as one chunk on the matrix cores
+// (HYPIC, codernav.top article, section on seam windows: the window's state
+// and outputs are computed on the fly).  With S0 the state entering the chunk,
+// a_t = e^{g_t}, e_t = a_0 .. a_t, D_ti = a_{i+1} .. a_t (t >= i),
+// lambda = e_{c-1}, ec_t = a_{t+1} .. a_{c-1}:
+//     Y = V - diag(e) K S0,   R = (I + N)^-1 diag(beta) Y,
+//     N_ti = beta_t (k_t . k_i) D_ti (t > i),
+//     o_t = e_t q_t^T S0 + sum_{i<=t} (q_t . k_i) D_ti R_i,
+//     S   = lambda S0 + K^T diag(ec) R,
+// which is the token recurrence S_t = a_t (I - beta_t k_t k_t^T) S_{t-1} +
+// beta_t k_t v_t^T, o_t = S_t^T q_t, regrouped.  Every decay factor is a
+// product of a's, so none exceeds 1.  Tokens past nt are zero tokens with
+// a = beta = 1.  sNw, sMw: this wave's 8 x 9 fp32 scratch.
+template <int D, int FAM>
+__device__ void seam_chunk_bf16(f32x4 (&X)[D / 16][2], const SeamSmem<D, FAM> &sm, int nt, float *o_first,
+                                int64_t o_tok_stride, int c0, int dk, float (*sNw)[9], float (*sMw)[9]) {
+    constexpr int RT = D / 16, KB = D / 32;
+    const int lane = lane_id(), r16 = lane & 15, grp = lane >> 4;
+    float a[SEAM_STAGE], eg[SEAM_STAGE], ec[SEAM_STAGE];
+#pragma unroll
+    for (int t = 0; t < SEAM_STAGE; ++t) a[t] = FAM == GDN ? sm.a[t][0] : 1.f;
+    {
+        float p = 1.f;
+#pragma unroll
+        for (int t = 0; t < SEAM_STAGE; ++t) eg[t] = p = p * a[t];
+        p = 1.f;
+#pragma unroll
+        for (int t = SEAM_STAGE - 1; t >= 0; --t) {
+            ec[t] = p;
+            p *= a[t];
+        }
+    }
+    const float lam = eg[SEAM_STAGE - 1];
+    // P = [K; Q] S0 (rows 0-7: K S0, rows 8-15: Q S0) and the Gram [K;Q][K;Q]^T
+    const float *qk = r16 < 8 ? &sm.k[r16][0] : &sm.q[r16 - 8][0];
+    f32x4 P[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 G = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        const f32x4 u = *reinterpret_cast<const f32x4 *>(qk + 32 * kb + 4 * grp);
+        const f32x4 w = *reinterpret_cast<const f32x4 *>(qk + 32 * kb + 16 + 4 * grp);
+        bf16x8 af;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            af[e] = (bf16)u[e];
+            af[4 + e] = (bf16)w[e];
+        }
+        G = mfma(af, af, G);
+#pragma unroll
+        for (int n2 = 0; n2 < 2; ++n2) {
+            float xv[8];
+            bf16x8 xh, xl;
+            acc_to_perm(X[2 * kb][n2], X[2 * kb + 1][n2], xv);
+            split8(xv, xh, xl);
+            P[n2] = mfma(af, xh, P[n2]);
+            P[n2] = mfma(af, xl, P[n2]);
+        }
+    }
+    // G in C layout: lane (r16 = i, grp) holds row 4 grp + jj.  Rows 0-7 give
+    // N (t > i), rows 8-15 give M (i <= t) for t = row - 8.
+    if (r16 < 8) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int row = 4 * grp + jj, t = row & 7, i = r16;
+            float dti = 1.f;
+#pragma unroll
+            for (int j = 1; j < SEAM_STAGE; ++j)
+                if (i < j && j <= t) dti *= a[j];
+            if (row < 8)
+                sNw[t][i] = t > i ? sm.beta[t] * G[jj] * dti : 0.f;
+            else
+                sMw[t][i] = i <= t ? G[jj] * dti : 0.f;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // row r16 of (I + N)^-1 diag(beta): y (I + N) = e_r, swept from the last row up
+    float y[SEAM_STAGE];
+#pragma unroll
+    for (int j = 0; j < SEAM_STAGE; ++j) y[j] = (j == r16) ? 1.f : 0.f;
+#pragma unroll
+    for (int i = SEAM_STAGE - 1; i > 0; --i)
+#pragma unroll
+        for (int j = 0; j < i; ++j) y[j] -= y[i] * sNw[i][j];
+    // (register arrays are indexed only with unrolled constants: lane group
+    // 0 takes entries 0-3, lane group 1 entries 4-7)
+    f32x4 arow = {0.f, 0.f, 0.f, 0.f}, mrow = {0.f, 0.f, 0.f, 0.f};
+    if (grp < 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = 4 * grp + e;
+            arow[e] = r16 < 8 ? (grp == 0 ? y[e] : y[4 + e]) * sm.beta[j] : 0.f;
+            mrow[e] = r16 >= 8 ? sMw[r16 - 8][j] : 0.f;
+        }
+    }
+    f32x4 eg4 = {eg[0], eg[1], eg[2], eg[3]}, ec4 = {ec[0], ec[1], ec[2], ec[3]};
+    if (grp & 1) {
+        eg4 = f32x4{eg[4], eg[5], eg[6], eg[7]};
+        ec4 = f32x4{ec[4], ec[5], ec[6], ec[7]};
+    }
+    s4v ah, al, mh, ml;
+    split4v(arow, ah, al);
+    split4v(mrow, mh, ml);
+#pragma unroll
+    for (int n2 = 0; n2 < 2; ++n2) {
+        const int col = c0 + 16 * n2 + r16;
+        // Y rows 0-7 (lane groups 0, 1); zero in rows 8-15
+        f32x4 yv = {0.f, 0.f, 0.f, 0.f};
+        if (grp < 2) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int t = 4 * grp + jj;
+                yv[jj] = sm.v[t][col < D ? col : D - 1] - eg4[jj] * P[n2][jj];
+            }
+        }
+        s4v yh, yl;
+        split4v(yv, yh, yl);
+        f32x4 R = {0.f, 0.f, 0.f, 0.f};
+        R = mfma16(ah, yh, R);
+        R = mfma16(ah, yl, R);
+        R = mfma16(al, yh, R);
+        s4v rh, rl;
+        split4v(R, rh, rl);
+        // outputs, rows 8-15: o_t = e_t (Q S0)_t + (M R)_t
+        f32x4 O = {0.f, 0.f, 0.f, 0.f};
+        O = mfma16(mh, rh, O);
+        O = mfma16(mh, rl, O);
+        O = mfma16(ml, rh, O);
+        if (grp >= 2 && col < dk) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int t = 4 * (grp - 2) + jj;
+                if (t < nt) o_first[t * o_tok_stride + col] = eg4[jj] * P[n2][jj] + O[jj];
+            }
+        }
+        // S = lambda S0 + K^T diag(ec) R  (R rows 8-15 are zero)
+        f32x4 Rs = R;
+        if (grp < 2) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) Rs[jj] *= ec4[jj];
+        }
+        split4v(Rs, rh, rl);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            s4v kt = {0, 0, 0, 0};
+            if (grp < 2)
+                kt = bf4(sm.k[4 * grp][16 * rt + r16], sm.k[4 * grp + 1][16 * rt + r16], sm.k[4 * grp + 2][16 * rt + r16],
+                         sm.k[4 * grp + 3][16 * rt + r16]);
+            f32x4 acc = X[rt][n2] * lam;
+            acc = mfma16(kt, rh, acc);
+            X[rt][n2] = mfma16(kt, rl, acc);
+        }
+    }
+}
+
+// Tile <- p[row * ld + c0 + c] (rows < nrows, columns c0 + c < ncols), zero
+// elsewhere.  The loads are unconditional (clamped indices, masked values), so
+// they are all in flight together.
 template <int D>
 __device__ __forceinline__ void load_tile(f32x4 (&X)[D / 16][2], const float *p, int ld, int nrows, int c0, int ncols) {
     const int lane = lane_id(), r16 = lane & 15, grp = lane >> 4;
@@ -150,7 +398,8 @@ __device__ __forceinline__ void load_tile(f32x4 (&X)[D / 16][2], const float *p,
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int row = 16 * rt + 4 * grp + jj, col = c0 + 16 * nt + r16;
-                X[rt][nt][jj] = (row < nrows && col < ncols) ? p[row * ld + col] : 0.f;
+                const float v = p[(row < nrows ? row : nrows - 1) * ld + (col < ncols ? col : ncols - 1)];
+                X[rt][nt][jj] = (row < nrows && col < ncols) ? v : 0.f;
             }
 }
 
@@ -184,11 +433,11 @@ __device__ __forceinline__ void store_tile(const f32x4 (&X)[D / 16][2], float *p
 // k block kb, zero outside dk.
 __device__ __forceinline__ void glb_perm(const float *M, int dk, int row, int kb, int grp, float (&x)[8]) {
     const int c0 = 32 * kb + 4 * grp, c1 = c0 + 16;
-    f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-    if (row < dk) {
-        if (c0 < dk) a = *reinterpret_cast<const f32x4 *>(M + row * dk + c0);
-        if (c1 < dk) b = *reinterpret_cast<const f32x4 *>(M + row * dk + c1);
-    }
+    const int rc = row < dk ? row : dk - 1;
+    f32x4 a = *reinterpret_cast<const f32x4 *>(M + rc * dk + (c0 < dk ? c0 : dk - 4));
+    f32x4 b = *reinterpret_cast<const f32x4 *>(M + rc * dk + (c1 < dk ? c1 : dk - 4));
+    if (!(row < dk && c0 < dk)) a = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (!(row < dk && c1 < dk)) b = f32x4{0.f, 0.f, 0.f, 0.f};
     x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
     x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
 }
@@ -234,10 +483,10 @@ __device__ __forceinline__ void apply_diag_T(f32x4 (&X)[D / 16][2], const float 
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int row = 16 * rt + 4 * grp + jj, col = c0 + 16 * nt + r16;
-                if (row < dk && col < dk) {
-                    const float tv = t_elems == 1 ? T[0] : T[row];
-                    X[rt][nt][jj] = tv * X[rt][nt][jj] + (add ? add[row * dk + col] : 0.f);
-                }
+                const int rc = row < dk ? row : dk - 1, cc = col < dk ? col : dk - 1;
+                const float tv = t_elems == 1 ? T[0] : T[rc];
+                const float av = add ? add[rc * dk + cc] : 0.f;
+                if (row < dk && col < dk) X[rt][nt][jj] = tv * X[rt][nt][jj] + av;
             }
 }
 
