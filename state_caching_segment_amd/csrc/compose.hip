@@ -142,6 +142,7 @@ k_compose_dense(ComposeArgs a) {
         const int idx = b + lane < m ? b + lane : m - 1;
         win_pid = a.pair_id[e0 + idx];
         win_sb = a.has_seam ? a.seam_begin[e0 + idx] : -1;
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): settled here, not at every later use
     };
     auto pid_at = [&](int j) -> int64_t { return __builtin_amdgcn_readlane(win_pid, j - win_base); };
     auto sb_at = [&](int j) -> int64_t {
@@ -218,8 +219,8 @@ k_compose_dense(ComposeArgs a) {
         t_load(0);
         s_load(0);
         t_put(0);
-        if (m > 1) t_load(1);
-        if (seam_one_stage && sb_at(0) >= 0) seam_fetch<D, FAM, TIN>(seam_pf, a.x, chain, dk, sb_at(0), a.w);
+        t_load(m > 1 ? 1 : 0);
+        if (seam_one_stage) seam_fetch<D, FAM, TIN>(seam_pf, a.x, chain, dk, sb_at(0), a.w);
         __syncthreads();
     }
     for (int j = 0; j < m; ++j) {
@@ -257,11 +258,11 @@ k_compose_dense(ComposeArgs a) {
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) X[rt][nt] = quad_transpose(spre[rt][nt], lane);
-            if (j + 1 < m) {
-                s_load(j + 1);
-                if (seam_one_stage && sb_at(j + 1) >= 0)
-                    seam_fetch<D, FAM, TIN>(seam_pf, a.x, chain, dk, sb_at(j + 1), a.w);
-            }
+            // (past the last entry these re-read the last one: the same loads on
+            // every path keep the compiler's wait counts exact)
+            const int jn = j + 1 < m ? j + 1 : j;
+            s_load(jn);
+            if (seam_one_stage) seam_fetch<D, FAM, TIN>(seam_pf, a.x, chain, dk, sb_at(jn), a.w);
             const float *tf = reinterpret_cast<const float *>(tsm[j & 1]);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
@@ -286,11 +287,9 @@ k_compose_dense(ComposeArgs a) {
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) X[rt][nt] = quad_transpose(spre[rt][nt], lane);
-            if (j + 1 < m) {
-                s_load(j + 1);
-                if (seam_one_stage && sb_at(j + 1) >= 0)
-                    seam_fetch<D, FAM, TIN>(seam_pf, a.x, chain, dk, sb_at(j + 1), a.w);
-            }
+            const int jn = j + 1 < m ? j + 1 : j;
+            s_load(jn);
+            if (seam_one_stage) seam_fetch<D, FAM, TIN>(seam_pf, a.x, chain, dk, sb_at(jn), a.w);
             const bf16 *th = reinterpret_cast<const bf16 *>(tsm[j & 1]);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
@@ -307,10 +306,8 @@ k_compose_dense(ComposeArgs a) {
                     }
                 }
         }
-        if (j + 1 < m) {
-            t_put((j + 1) & 1);  // that buffer's last readers finished entry j - 1
-            if (j + 2 < m) t_load(j + 2);
-        }
+        if (j + 1 < m) t_put((j + 1) & 1);  // that buffer's last readers finished entry j - 1
+        t_load(j + 2 < m ? j + 2 : m - 1);
         __syncthreads();
     }
     store_tile<D>(X, st, dk, dk, c0, dk);

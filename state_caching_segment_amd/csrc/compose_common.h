@@ -174,17 +174,53 @@ struct SeamPrefetch {
     TIN g, b;
 };
 
+// A raw buffer view of nbytes from p (p wave-uniform); reads past nbytes return
+// zero without touching memory, so a view of 0 bytes reads as all zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const void *p, int nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, nbytes, 0x00020000);
+}
+
+template <typename TIN>
+__device__ __forceinline__ TIN buffer_scalar(__amdgpu_buffer_rsrc_t r, int off) {
+    if constexpr (std::is_same<TIN, float>::value)
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    else
+        return __builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
+
+// Fetch the seam stage of tokens tok0 .. tok0 + nt - 1 of `chain`; when the
+// entry has no seam (tok0 < 0) every view is empty and the registers read as
+// zero.  The loads are the same on every path, so the compiler can count
+// them and later waits cover only what they need.
 template <int D, int FAM, typename TIN>
 __device__ __forceinline__ void seam_fetch(SeamPrefetch<D, TIN> &p, const Tok &x, int chain, int dk, int64_t tok0, int nt) {
     using V4 = typename SeamPrefetch<D, TIN>::V4;
     const int tid = threadIdx.x, t = tid / (D / 4), i = 4 * (tid % (D / 4));
-    const int64_t tc = tok0 + (t < nt ? t : nt - 1);
-    const int64_t off = (int64_t)chain * x.cs + tc * x.ts + (i < dk ? i : dk - 4);
-    p.q = *reinterpret_cast<const V4 *>(reinterpret_cast<const TIN *>(x.q) + off);
-    p.k = *reinterpret_cast<const V4 *>(reinterpret_cast<const TIN *>(x.k) + off);
-    p.v = *reinterpret_cast<const V4 *>(reinterpret_cast<const TIN *>(x.v) + off);
-    if (fam_sgate(FAM)) p.g = reinterpret_cast<const TIN *>(x.g)[(int64_t)chain * x.gcs + tc * x.gts];
-    if (fam_beta(FAM)) p.b = reinterpret_cast<const TIN *>(x.beta)[(int64_t)chain * x.bcs + tc * x.bts];
+    const bool on = tok0 >= 0;
+    const int64_t tb = on ? tok0 : 0;
+    const int row_bytes = (int)(((int64_t)(nt - 1) * x.ts + dk) * sizeof(TIN));
+    const int off = (int)(((int64_t)t * x.ts + i) * sizeof(TIN));
+    const int64_t base = (int64_t)chain * x.cs + tb * x.ts;
+    auto ld4 = [&](const void *ptr) -> V4 {
+        const auto r = buffer_view(reinterpret_cast<const TIN *>(ptr) + base, on ? row_bytes : 0);
+        if constexpr (std::is_same<TIN, float>::value)
+            return __builtin_bit_cast(V4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+        else
+            return __builtin_bit_cast(V4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    };
+    p.q = ld4(x.q);
+    p.k = ld4(x.k);
+    p.v = ld4(x.v);
+    if (fam_sgate(FAM)) {
+        const auto r = buffer_view(reinterpret_cast<const TIN *>(x.g) + (int64_t)chain * x.gcs + tb * x.gts,
+                                   on ? (int)(((int64_t)(nt - 1) * x.gts + 1) * sizeof(TIN)) : 0);
+        p.g = buffer_scalar<TIN>(r, (int)((int64_t)t * x.gts * sizeof(TIN)));
+    }
+    if (fam_beta(FAM)) {
+        const auto r = buffer_view(reinterpret_cast<const TIN *>(x.beta) + (int64_t)chain * x.bcs + tb * x.bts,
+                                   on ? (int)(((int64_t)(nt - 1) * x.bts + 1) * sizeof(TIN)) : 0);
+        p.b = buffer_scalar<TIN>(r, (int)((int64_t)t * x.bts * sizeof(TIN)));
+    }
 }
 
 // Write a fetched stage into the LDS staging area (zero tokens past nt).
