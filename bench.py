@@ -80,6 +80,13 @@ def build_kernel(family, dtype):
     return "k_build_diag", ["build_diag.hip", "common.h"]
 
 
+def compose_kernel(family):
+    """The sequential compose kernel the library dispatches for a family, and
+    the sources whose hash keys its stored counter readings."""
+    files = ["compose.hip", "compose_common.h", "common.h"]
+    return ("k_compose_dense" if family in ("deltanet", "gdn", "kda") else "k_compose_seq"), files
+
+
 def measured_traffic(key, files):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     passes (profiles/counters.json), or None when the kernel's source changed
@@ -218,9 +225,10 @@ def main():
     roof_build.update({"traffic": measured_traffic("build", bk_files),
                        "kernel": bk_name, "alg_bytes": bb, "alg_flops": bf,
                        "mfma_frac_alg": b_mfma / BF16_PEAK, "hbm_frac_alg": b_hbm / HBM_PEAK})
+    ck_name, ck_files = compose_kernel(wl.family)
     roof_comp = {"bound": "hbm", "achieved": cb / tc / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                 "frac": cb / tc / HBM_PEAK, "traffic": measured_traffic("compose", ["compose.hip", "common.h"]),
-                 "kernel": "k_compose_seq", "alg_bytes": cb,
+                 "frac": cb / tc / HBM_PEAK, "traffic": measured_traffic("compose", ck_files),
+                 "kernel": ck_name, "alg_bytes": cb,
                  "alg_flops": cf}
     out = {
         "metric": METRIC,
