@@ -39,32 +39,53 @@ FP32_MFMA_PEAK = 157.3e12
 CH = 64
 
 
-def build_cost(lens, d, n_chains, in_bytes):
+DENSE = ("deltanet", "gdn", "kda")
+
+
+def _gate_elems(family, d):
+    """Log-gate values per token: a dk-vector (GLA, KDA), a scalar (Mamba2,
+    GDN) or none."""
+    return d if family in ("gla", "kda") else (1 if family in ("mamba2", "gdn") else 0)
+
+
+def _t_elems(family, d):
+    return d * d if family in DENSE else (d if family == "gla" else 1)
+
+
+def build_cost(family, lens, d, n_chains, in_bytes):
     """Algorithmic flops and HBM bytes of building the pairs of segments with
-    the given lengths (chunked UT/WY form, c = 64):
-      per chunk of c tokens: carry of [T|S] 8 c d^2 (4 c d^2 for a segment's
-      first chunk, which starts from [I|0]), Gram c(c-1)d, unit-lower inverse
-      c^3/3, W and U 2 c^2 d;
-      bytes: k, v (d each), g and beta (1 each) per token read once, and the
-      fp32 pair (T and S, d^2 each) written once."""
+    the given lengths.
+    Dense families (chunked UT/WY form, c = 64), per chunk of c tokens: carry
+    of [T|S] 8 c d^2 (4 c d^2 for a segment's first chunk, which starts from
+    [I|0]), Gram c(c-1)d, unit-lower inverse c^3/3, W and U 2 c^2 d.
+    Diagonal families: 2 d^2 per token (the k~ v^T accumulation).
+    Bytes: k, v (d each), the log-gates and beta per token read once, and the
+    fp32 pair (T and S) written once."""
     flops = 0.0
     for n in lens:
-        for j, c0 in enumerate(range(0, int(n), CH)):
-            c = min(CH, int(n) - c0)
-            carry = 8 * c * d * d if j > 0 else 4 * c * d * d
-            flops += carry + c * (c - 1) * d + c ** 3 / 3 + 2 * c * c * d
+        if family in DENSE:
+            for j, c0 in enumerate(range(0, int(n), CH)):
+                c = min(CH, int(n) - c0)
+                carry = 8 * c * d * d if j > 0 else 4 * c * d * d
+                flops += carry + c * (c - 1) * d + c ** 3 / 3 + 2 * c * c * d
+        else:
+            flops += 2.0 * d * d * int(n)
     tokens = float(np.sum(lens))
-    byts = tokens * (2 * d + 2) * in_bytes + len(lens) * 2 * d * d * 4
+    per_tok = 2 * d + _gate_elems(family, d) + (1 if family in DENSE else 0)
+    byts = tokens * per_tok * in_bytes + len(lens) * (_t_elems(family, d) + d * d) * 4
     return flops * n_chains, byts * n_chains
 
 
-def compose_cost(n_entries, n_seams, w, d, n_chains, in_bytes):
+def compose_cost(family, n_entries, n_seams, w, d, n_chains, in_bytes):
     """Algorithmic flops and bytes of one sequential compose with seams: every
-    pair read once (fp32 T and S), per seam token q, k, v (d each), g and beta
-    read and o (d, fp32) written, initial and final state; flops 2 d^3 per
-    pair after the first (T S) and ~7 d^2 per seam token."""
-    flops = (n_entries - 1) * 2 * d ** 3 + n_seams * w * 7 * d * d
-    byts = n_entries * 2 * d * d * 4 + n_seams * w * ((3 * d + 2) * in_bytes + d * 4) + 2 * d * d * 4
+    pair read once (fp32 T and S), per seam token q, k, v (d each), the gates
+    and beta read and o (d, fp32) written, initial and final state; flops
+    2 d^3 per dense pair after the first (T S; 2 d^2 for diagonal T) and
+    about 7 d^2 per seam token."""
+    pair_flops = 2 * d ** 3 if family in DENSE else 2 * d * d
+    flops = (n_entries - 1) * pair_flops + n_seams * w * 7 * d * d
+    seam_in = 3 * d + _gate_elems(family, d) + (1 if family in DENSE else 0)
+    byts = n_entries * (_t_elems(family, d) + d * d) * 4 + n_seams * w * (seam_in * in_bytes + d * 4) + 2 * d * d * 4
     return flops * n_chains, byts * n_chains
 
 
@@ -132,6 +153,17 @@ def cpu_baseline(wl, n_chains_sample, w):
                       f"(all pairs + compose + seams), {dt:.1f} s; scaled by chains"}
 
 
+def workload_text(name, wl, plan, C, d, w, req_tokens, n_build, hits):
+    n_req = len(wl.requests)
+    heads = "30 layers x 32 heads" if C == 960 else f"{C} heads"
+    req = (f"one {req_tokens}-token request" if n_req == 1 else f"{n_req} requests, {req_tokens} tokens")
+    if hits:
+        return (f"{wl.family} {wl.dtype}: build of {n_build} cold segment bodies + tree compose with w={w} seams "
+                f"over all {plan.n_slots} cached pairs: {C} chains ({heads}), d={d}, {req}")
+    return (f"{wl.family} pair build + seq compose with w={w} seams: {C} chains ({heads}), d={d}, {req}, "
+            f"{plan.n_slots} segments")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,18 +212,43 @@ def main():
     state = torch.zeros(plan.n_req, C, d, d, device=dev)
     o = torch.zeros(len(plan.pair_id), w, C, d, device=dev)
     stream = torch.cuda.current_stream()
+    # Workloads with cache hits (n_cold set) time the build of the cold
+    # segment bodies only, into their own pair buffers, and compose with the
+    # associative tree scan over the full pair cache, which is built once
+    # beforehand (untimed); the others time the build of every segment and
+    # the sequential compose.
+    cold = np.concatenate([c for c in wl.cold]) if wl.cold else np.ones(plan.n_slots, bool)
+    hits = not cold.all()
+    mode = hy.TREE if hits else hy.SEQ
+    if hits:
+        hy.hypic_segment_build(L, x, plan.n_slots, sb, se, plan.max_seg_len, T, S, stream=stream)
+        cb_idx = np.nonzero(cold)[0]
+        bsb = torch.from_numpy(plan.seg_begin[cb_idx]).to(dev)
+        bse = torch.from_numpy(plan.seg_end[cb_idx]).to(dev)
+        n_build = len(cb_idx)
+        bT = torch.empty(n_build, C, te, device=dev)
+        bS = torch.empty(n_build, C, d, d, device=dev)
+        build_lens = plan.seg_end[cb_idx] - plan.seg_begin[cb_idx]
+    else:
+        bsb, bse, n_build, bT, bS = sb, se, plan.n_slots, T, S
+        build_lens = plan.seg_end - plan.seg_begin
+    max_build = int(build_lens.max())
+    ws, nws = None, 0
+    if mode == hy.TREE:
+        nws = hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, plan.n_req, plan.max_list_len, w)
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
 
-    def step(ev=None):
+    def step(ev=None, cmode=mode):
         if ev:
             ev[0].record(stream)
-        hy.hypic_segment_build(L, x, plan.n_slots, sb, se, plan.max_seg_len, T, S, stream=stream)
+        hy.hypic_segment_build(L, x, n_build, bsb, bse, max_build, bT, bS, stream=stream)
         if ev:
             ev[1].record(stream)
         state.zero_()
         if ev:
             ev[2].record(stream)
-        hy.hypic_compose(L, hy.SEQ, plan.n_req, plan.max_list_len, lo, pid, plan.n_slots, T, S, x, seam, w, state,
-                         o, stream=stream)
+        hy.hypic_compose(L, cmode, plan.n_req, plan.max_list_len, lo, pid, plan.n_slots, T, S, x, seam, w, state,
+                         o, ws if cmode == hy.TREE else None, nws if cmode == hy.TREE else 0, stream=stream)
         if ev:
             ev[3].record(stream)
 
@@ -204,15 +261,23 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    seq_ms = None
+    if mode == hy.TREE:  # the sequential compose of the same lists, for comparison
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            step(sev[i], hy.SEQ)
+        torch.cuda.synchronize()
+        seq_ms = float(np.median([e[2].elapsed_time(e[3]) for e in sev]))
     b_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     c_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
     step_ms = wall * 1e3 / args.steps
 
     in_bytes = 2 if wl.dtype == "bf16" else 4
-    req_tokens = int(wl.requests[0][-1] - wl.requests[0][0])
-    bf, bb = build_cost(plan.seg_end - plan.seg_begin, d, C, in_bytes)
+    req_tokens = int(sum(int(b[-1] - b[0]) for b in wl.requests))
+    build_tokens = int(build_lens.sum())
+    bf, bb = build_cost(wl.family, build_lens, d, C, in_bytes)
     n_seams = int((plan.seam_begin >= 0).sum())
-    cf, cb = compose_cost(len(plan.pair_id), n_seams, w, d, C, in_bytes)
+    cf, cb = compose_cost(wl.family, len(plan.pair_id), n_seams, w, d, C, in_bytes)
     tb, tc = float(np.median(b_ms)) * 1e-3, float(np.median(c_ms)) * 1e-3
     # the build's binding roof is the larger of its HBM and bf16-MFMA times
     b_hbm, b_mfma = bb / tb, bf / tb
@@ -222,17 +287,18 @@ def main():
                   {"bound": "mfma", "achieved": b_mfma / 1e12, "peak": BF16_PEAK / 1e12, "unit": "TFLOP/s",
                    "frac": b_mfma / BF16_PEAK})
     bk_name, bk_files = build_kernel(wl.family, wl.dtype)
-    roof_build.update({"traffic": measured_traffic("build", bk_files),
+    key = "" if args.config == "c4" else "_" + args.config  # stored counters per workload
+    roof_build.update({"traffic": measured_traffic("build" + key, bk_files),
                        "kernel": bk_name, "alg_bytes": bb, "alg_flops": bf,
                        "mfma_frac_alg": b_mfma / BF16_PEAK, "hbm_frac_alg": b_hbm / HBM_PEAK})
     ck_name, ck_files = compose_kernel(wl.family)
     roof_comp = {"bound": "hbm", "achieved": cb / tc / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                 "frac": cb / tc / HBM_PEAK, "traffic": measured_traffic("compose", ck_files),
+                 "frac": cb / tc / HBM_PEAK, "traffic": measured_traffic("compose" + key, ck_files),
                  "kernel": ck_name, "alg_bytes": cb,
                  "alg_flops": cf}
     out = {
         "metric": METRIC,
-        "value": req_tokens / tb,
+        "value": build_tokens / tb,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -243,19 +309,20 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": f"{wl.family} pair build + seq compose with w={w} seams: {C} chains "
-                               f"(30 layers x 32 heads), d={d}, one {req_tokens}-token request, "
-                               f"{plan.n_slots} segments",
+        "config": {"workload": workload_text(args.config, wl, plan, C, d, w, req_tokens, n_build, hits),
                    "chains": C, "d": d, "request_tokens": req_tokens, "segments": plan.n_slots, "w": w,
+                   "built_segments": n_build, "built_tokens": build_tokens, "compose_mode": "tree" if hits else "seq",
                    "state_dtype": "f32"},
         "build_ms": float(np.median(b_ms)),
         "build_ms_p10_p90": [float(np.percentile(b_ms, 10)), float(np.percentile(b_ms, 90))],
         "compose_latency_ms": float(np.median(c_ms)),
         "compose_ms_p10_p90": [float(np.percentile(c_ms, 10)), float(np.percentile(c_ms, 90))],
-        "chain_tokens_per_s_build": req_tokens * C / tb,
+        "chain_tokens_per_s_build": build_tokens * C / tb,
         "roofline": roof_build,
         "roofline_compose": roof_comp,
     }
+    if seq_ms is not None:
+        out["compose_seq_latency_ms"] = seq_ms
     if args.cpu_chains != 0:
         import oracle
         n_cpu = 2 * oracle.max_threads() if args.cpu_chains < 0 else args.cpu_chains

@@ -224,6 +224,271 @@ k_build_diag(BuildArgs a) {
     }
 }
 
+// ---- bf16 inputs: four token slices of a segment in parallel -----------------
+//
+// The state of a diagonal-decay segment is a sum over its tokens,
+//     S = sum_t diag(e^{Gamma_end - Gamma_t}) k_t v_t^T,
+// so a segment splits into slices whose partial states combine in order,
+//     S = L_3 (L_2 (L_1 S_0 + S_1) + S_2) + S_3,
+// L_g the slice's decay product (one value per key channel).  One workgroup
+// per (segment, chain) holds four slice groups of d/32 waves each; group g
+// streams its quarter of the segment in 32-token chunks, last chunk first, so
+// the decay from a token to the slice's end is a product of per-token gates
+// that is known when the token is staged: within the chunk, a suffix product
+// over the lane's 8 tokens and across the 4 lanes holding the chunk's quarters;
+// beyond it, D, the running product over the chunks already done.  All these
+// factors are at most 1.  The staging lanes (one channel pair and one quarter
+// of the chunk's tokens each) write K~ = k * decay (hi and lo bf16) and V rows
+// to LDS; each wave then adds K~^T V into its 32 columns of the slice state on
+// the matrix cores, through transpose reads.  At the end the slice states are
+// combined through LDS; T = exp(sum of the segment's log-gates).
+template <int D>
+struct SliceCfg {
+    static constexpr int NW = D / 32;  // waves per slice group (one per 32 columns / 32 channels)
+    static constexpr int NG = 4;       // slice groups
+    static constexpr int NT = NG * NW * 64;
+    static constexpr int CS = 32;      // tokens per chunk
+    static constexpr int LDK = D + 8;  // bf16 row stride of K~ and V rows
+    static constexpr int al(int x) { return (x + 15) / 16 * 16; }
+    static constexpr int gK = 0;
+    static constexpr int gKl = gK + al(CS * LDK * 2);
+    static constexpr int gV = gKl + al(CS * LDK * 2);
+    static constexpr int GRP = al(gV + CS * LDK * 2);
+    static constexpr int LDS_ = D + 4;  // fp32 row stride of the combine's S
+    static constexpr int cS = 0, cTot = al(D * LDS_ * 4);
+    static constexpr int total = (NG * GRP > cTot + NG * D * 4) ? NG * GRP : cTot + NG * D * 4;
+    static_assert(total <= 160 * 1024, "LDS budget");
+};
+
+template <int D, int FAM>
+__global__ void __launch_bounds__(4 * (D / 32) * 64)
+k_build_diag_slices(BuildArgs a) {
+    using Cfg = SliceCfg<D>;
+    constexpr int NW = Cfg::NW, NG = Cfg::NG, RT = D / 16, CS = Cfg::CS, LDK = Cfg::LDK;
+    constexpr float L2E = 1.4426950408889634f;
+    constexpr bool VG = FAM == GLA;                      // a log-gate per channel
+    constexpr bool DEC = FAM != LINEAR;                  // any decay
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::total];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int gi = wv / NW, q = wv % NW;  // slice group; column block (carry) = channel block (staging)
+    const int r16 = lane & 15, grp = lane >> 4;
+    const int seg = blockIdx.x / a.n_chains, chain = blockIdx.x % a.n_chains;
+    const int dk = a.dk;
+    const int64_t b0 = a.seg_begin[seg], n = a.seg_end[seg] - b0;
+    const int nch = (int)((n + CS - 1) / CS);
+    const int per = (nch + NG - 1) / NG;  // chunks per slice group
+    char *gb = smem + gi * Cfg::GRP;
+    bf16 *sK = reinterpret_cast<bf16 *>(gb + Cfg::gK);
+    bf16 *sKl = reinterpret_cast<bf16 *>(gb + Cfg::gKl);
+    bf16 *sV = reinterpret_cast<bf16 *>(gb + Cfg::gV);
+
+    // staging role: channels ch, ch + 1 and tokens 8 tq .. 8 tq + 7 of the chunk
+    const int tq = lane >> 4, ch = 32 * q + 2 * (lane & 15);
+    const bool ch_ok = ch < dk;
+    const int chc = ch_ok ? ch : 0;
+    const bf16 *kp = reinterpret_cast<const bf16 *>(a.x.k) + (int64_t)chain * a.x.cs + chc;
+    const bf16 *vp = reinterpret_cast<const bf16 *>(a.x.v) + (int64_t)chain * a.x.cs + chc;
+    const bf16 *gp = (VG || FAM == MAMBA2)
+                         ? reinterpret_cast<const bf16 *>(a.x.g) + (int64_t)chain * a.x.gcs + (VG ? chc : 0)
+                         : nullptr;
+    const float lgam = FAM == RETNET ? logf(a.x.gamma[chain]) * L2E : 0.f;
+
+    typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 pk[8], pv[8], pg[8];
+    bf16 pgs[8];
+    int pvalid = 0;  // bit j: token 8 tq + j of the prefetched chunk exists
+    // chunk gc of the segment into the prefetch registers (unconditional loads
+    // from clamped tokens, masked when used)
+    auto fetch = [&](int gc) {
+        pvalid = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t tok = (int64_t)gc * CS + 8 * tq + j;
+            if (gc >= 0 && gc < nch && tok < n && ch_ok) pvalid |= 1 << j;
+            const int64_t tc = b0 + (tok < n ? (tok >= 0 ? tok : 0) : (n > 0 ? n - 1 : 0));
+            pk[j] = *reinterpret_cast<const bf16x2 *>(kp + tc * a.x.ts);
+            pv[j] = *reinterpret_cast<const bf16x2 *>(vp + tc * a.x.ts);
+            if (VG) pg[j] = *reinterpret_cast<const bf16x2 *>(gp + tc * a.x.gts);
+            if (FAM == MAMBA2) pgs[j] = gp[tc * a.x.gts];
+        }
+    };
+
+    f32x4 X[RT][2];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) X[rt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float Dd[2] = {1.f, 1.f};    // decay from the end of the chunk being staged to the slice's end
+    float gsum[2] = {0.f, 0.f};  // summed log2-gates of this lane's tokens over the slice
+
+    const int first = gi * per + per - 1;  // chunks run last to first
+    if (per > 0) fetch(first);
+    for (int c = 0; c < per; ++c) {
+        const int gc = first - c;
+        // ---- this lane's quarter: product of its 8 tokens' gates per channel
+        auto gate = [&](int j, int e) -> float {
+            if (!(pvalid & (1 << j))) return 0.f;
+            return VG ? (float)pg[j][e] * L2E : (FAM == MAMBA2 ? (float)pgs[j] * L2E : lgam);
+        };
+        float P[2] = {1.f, 1.f};
+        if (DEC) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const float g = gate(j, e);
+                    gsum[e] += g;
+                    P[e] *= __builtin_amdgcn_exp2f(g);
+                }
+        }
+        // the later quarters' products (lanes + 16, + 32, + 48 hold them)
+        float E[2] = {1.f, 1.f};
+        if (DEC) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const float p1 = __shfl_down(P[e], 16), p2 = __shfl_down(P[e], 32), p3 = __shfl_down(P[e], 48);
+                E[e] = (tq < 3 ? p1 : 1.f) * (tq < 2 ? p2 : 1.f) * (tq < 1 ? p3 : 1.f) * Dd[e];
+            }
+        }
+        // ---- stage K~ = k * decay (hi, lo) and V rows, last token first:
+        // the decay of token j is E times the gates of the tokens after it
+        float W[2] = {E[0], E[1]};
+#pragma unroll
+        for (int j = 7; j >= 0; --j) {
+            const bool ok = pvalid & (1 << j);
+            float kv[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                kv[e] = ok ? (float)pk[j][e] * W[e] : 0.f;
+                if (DEC) W[e] *= __builtin_amdgcn_exp2f(gate(j, e));
+            }
+            const bf16 h0 = (bf16)kv[0], h1 = (bf16)kv[1];
+            const bf16x2 hh = {h0, h1};
+            const bf16x2 ll = {(bf16)(kv[0] - (float)h0), (bf16)(kv[1] - (float)h1)};
+            const bf16x2 vv = ok ? pv[j] : bf16x2{(bf16)0.f, (bf16)0.f};
+            const int o = (8 * tq + j) * LDK + ch;
+            *reinterpret_cast<bf16x2 *>(sK + o) = hh;
+            if (DEC) *reinterpret_cast<bf16x2 *>(sKl + o) = ll;
+            *reinterpret_cast<bf16x2 *>(sV + o) = vv;
+        }
+        // the chunk's whole decay joins D for the chunks before it
+        // (quarter 0's W now spans the whole chunk and the chunks after it)
+        if (DEC) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) Dd[e] = __shfl(W[e], r16);
+        }
+        __syncthreads();
+        fetch(gc - 1);
+        // ---- carry: S_g += K~^T V for columns 32q .. 32q+31
+        bf16x8 vb[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const bf16x4 u = lds_tr4(sV, LDK, 4 * grp, 32 * q + 16 * nt, r16);
+            const bf16x4 v = lds_tr4(sV, LDK, 16 + 4 * grp, 32 * q + 16 * nt, r16);
+            vb[nt] = bf16x8{u[0], u[1], u[2], u[3], v[0], v[1], v[2], v[3]};
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const bf16x8 kh = lds_tr_perm(sK, LDK, 0, 16 * rt, r16, grp);
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) X[rt][nt] = mfma(kh, vb[nt], X[rt][nt]);
+            if (DEC) {
+                const bf16x8 kl = lds_tr_perm(sKl, LDK, 0, 16 * rt, r16, grp);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) X[rt][nt] = mfma(kl, vb[nt], X[rt][nt]);
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- combine the slice states in order through LDS
+    float *cS = reinterpret_cast<float *>(smem + Cfg::cS);
+    float *cTot = reinterpret_cast<float *>(smem + Cfg::cTot);  // [NG][D] summed log2-gates
+    constexpr int LDS_ = Cfg::LDS_;
+    // the slice's log2-gate sum per channel: over the 4 quarters of this channel pair
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        gsum[e] += __shfl_xor(gsum[e], 16);
+        gsum[e] += __shfl_xor(gsum[e], 32);
+    }
+    if (tq == 0) {
+        if (VG) {
+            cTot[gi * D + ch] = gsum[0];
+            cTot[gi * D + ch + 1] = gsum[1];
+        } else if (lane == 0 && q == 0) {
+            cTot[gi * D] = gsum[0];
+        }
+    }
+    __syncthreads();
+    for (int g = 0; g < NG; ++g) {
+        if (gi == g) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int row = 16 * rt + 4 * grp + jj, col = 32 * q + 16 * nt + r16;
+                        float v = X[rt][nt][jj];
+                        if (g > 0) v += __builtin_amdgcn_exp2f(cTot[g * D + (VG ? row : 0)]) * cS[row * LDS_ + col];
+                        X[rt][nt][jj] = v;
+                        if (g < NG - 1) cS[row * LDS_ + col] = v;
+                    }
+        }
+        __syncthreads();
+    }
+    if (gi == NG - 1) {
+        float *So = a.S + ((int64_t)seg * a.n_chains + chain) * dk * dk;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int row = 16 * rt + 4 * grp + jj, col = 32 * q + 16 * nt + r16;
+                    if (row < dk && col < dk) So[row * dk + col] = X[rt][nt][jj];
+                }
+    }
+    if (gi == 0) {
+        const int tq2 = q * 64 + lane;
+        if (VG) {
+            for (int i = tq2; i < dk; i += NW * 64) {
+                float s2 = 0.f;
+                for (int g = 0; g < NG; ++g) s2 += cTot[g * D + i];
+                a.T[((int64_t)seg * a.n_chains + chain) * dk + i] = __builtin_amdgcn_exp2f(s2);
+            }
+        } else if (tq2 == 0) {
+            float tv = 1.f;
+            if (FAM == RETNET) tv = (float)pow((double)a.x.gamma[chain], (double)n);
+            if (FAM == MAMBA2) {
+                float s2 = 0.f;
+                for (int g = 0; g < NG; ++g) s2 += cTot[g * D];
+                tv = exp2f(s2);
+            }
+            a.T[(int64_t)seg * a.n_chains + chain] = tv;
+        }
+    }
+}
+
+template <int D, int FAM>
+static hipError_t launch_slices(const BuildArgs &a, int n_seg, hipStream_t st) {
+    const dim3 grid((unsigned)(n_seg * (int64_t)a.n_chains));
+    hipLaunchKernelGGL((k_build_diag_slices<D, FAM>), grid, dim3(SliceCfg<D>::NT), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int FAM>
+static hipError_t launch_slices_d(const BuildArgs &a, int D, int n_seg, hipStream_t st) {
+    switch (D) {
+    case 32: return launch_slices<32, FAM>(a, n_seg, st);
+    case 64: return launch_slices<64, FAM>(a, n_seg, st);
+    case 128: return launch_slices<128, FAM>(a, n_seg, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int D, int FAM, typename TIN>
 static hipError_t launch_diag(const BuildArgs &a, int n_seg, hipStream_t st) {
     const dim3 grid((unsigned)(n_seg * (int64_t)a.n_chains));
@@ -253,7 +518,14 @@ static hipError_t diag_by_family(const BuildArgs &a, int family, int D, int n_se
 }
 
 hipError_t build_diag(const BuildArgs &a, int family, bool bf16_in, int D, int n_seg, hipStream_t st) {
-    return bf16_in ? diag_by_family<bf16>(a, family, D, n_seg, st) : diag_by_family<float>(a, family, D, n_seg, st);
+    if (!bf16_in) return diag_by_family<float>(a, family, D, n_seg, st);
+    switch (family) {
+    case LINEAR: return launch_slices_d<LINEAR>(a, D, n_seg, st);
+    case RETNET: return launch_slices_d<RETNET>(a, D, n_seg, st);
+    case MAMBA2: return launch_slices_d<MAMBA2>(a, D, n_seg, st);
+    case GLA: return launch_slices_d<GLA>(a, D, n_seg, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace hy

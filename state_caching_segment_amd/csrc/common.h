@@ -85,6 +85,29 @@ __device__ __forceinline__ bf16x8 lds_cont(const bf16 *M, int ld, int row, int k
 }
 
 // Gather the permuted-k B operand of one 32-row k block from two stacked
+typedef short s4 __attribute__((ext_vector_type(4)));
+
+// 4 consecutive rows k0 .. k0+3 of column c0 + r16 of a row-major bf16 LDS
+// matrix (all 16 lanes of a lane group pass the same k0 and c0): the gfx950
+// transpose read, where source lane 4m + q supplies row k0 + m, columns
+// c0 + 4q .. c0 + 4q + 3.
+__device__ __forceinline__ bf16x4 lds_tr4(const bf16 *M, int ld, int k0, int c0, int r16) {
+    const bf16 *p = M + (k0 + (r16 >> 2)) * ld + c0 + 4 * (r16 & 3);
+    const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4 *)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+// permuted-k A fragment of row-major M transposed: rows = columns c0 + r16 of
+// M, k = rows kbase + {4grp .. 4grp+3, 16+4grp .. 16+4grp+3}
+__device__ __forceinline__ bf16x8 lds_tr_perm(const bf16 *M, int ld, int kbase, int c0, int r16, int grp) {
+    const bf16x4 a = lds_tr4(M, ld, kbase + 4 * grp, c0, r16);
+    const bf16x4 b = lds_tr4(M, ld, kbase + 16 + 4 * grp, c0, r16);
+    bf16x8 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+    r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+    return r;
+}
+
 // C-layout accumulator tiles (rows 0..15 in `top`, rows 16..31 in `bot`).
 __device__ __forceinline__ void acc_to_perm(const f32x4 &top, const f32x4 &bot, float (&x)[8]) {
     x[0] = top[0]; x[1] = top[1]; x[2] = top[2]; x[3] = top[3];

@@ -77,7 +77,7 @@ def test_slow_gate_gdn_d128():
 
 
 @pytest.mark.parametrize("fam", ["linear", "retnet", "mamba2", "gla"])
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("f32", 16), ("bf16", 32)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 16), ("bf16", 32), ("bf16", 16)])
 def test_diagonal_families(fam, dtype, d):
     gpu, _ = check(small(fam, dtype, d))
 
