@@ -111,27 +111,48 @@ struct DenseTLds {
     static constexpr int BYTES = D * LDT * (F32 ? 4 : 2);
 };
 
-template <int D, int FAM, typename TIN>
-__global__ void __launch_bounds__(D / 32 * 64)
-k_compose_dense(ComposeArgs a) {
+// TREE: the first phase of the tree compose on the same machinery.  The
+// workgroup owns one (request, block of entries, chain) and runs the block's
+// entries from (I, 0) on [T_p | S_p] with 2d/32 waves: the T half takes no
+// S_j and, at seams, zero values, so its seam read-out is the pulled-back
+// query T_p^T q_t; the block aggregate is written at the end.
+template <int D, int FAM, typename TIN, bool TREE>
+__global__ void __launch_bounds__((TREE ? 2 : 1) * D / 32 * 64)
+k_compose_dense(TreeArgs t) {
+    const ComposeArgs &a = t.c;
     constexpr bool F32 = std::is_same<TIN, float>::value;
     constexpr int NW = D / 32, RT = D / 16, KB = D / 32;
+    constexpr int NWT = (TREE ? 2 : 1) * NW;  // waves in the workgroup
     using TL = DenseTLds<D, F32>;
     constexpr int LDT = TL::LDT;
-    constexpr int NV = D * D / 4 / 64 / NW;  // 16-byte pieces of T per lane
-    constexpr int RPW = D / NW;              // T rows staged by one wave
+    constexpr int NV = D * D / 4 / 64 / NWT;  // 16-byte pieces of T per lane
+    constexpr int RPW = D / NWT;              // T rows staged by one wave
     __shared__ __attribute__((aligned(16))) char tsm[2][TL::BYTES];
     __shared__ SeamSmem<D, FAM> sm;
     constexpr bool CHUNK_SEAM = !F32 && (FAM == DELTANET || FAM == GDN);
-    __shared__ float seam_nm[CHUNK_SEAM ? NW : 1][2][SEAM_STAGE][9];
+    __shared__ float seam_nm[CHUNK_SEAM ? NWT : 1][2][SEAM_STAGE][9];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
-    const int req = blockIdx.x / a.n_chains, chain = blockIdx.x % a.n_chains;
+    const int chain = blockIdx.x % a.n_chains;
+    int req, j0 = 0, blk = 0;
+    if (TREE) {
+        const int rb = blockIdx.x / a.n_chains;
+        req = rb / t.NB;
+        blk = rb % t.NB;
+        j0 = blk * t.B;
+    } else {
+        req = blockIdx.x / a.n_chains;
+    }
+    const bool isS = !TREE || wv >= NW;  // owns S columns (else T columns)
     // d = 64 and d = 128 run unpadded (dk == D), which makes every offset below
     // a compile-time constant off one per-lane base
-    const int dk = D >= 64 ? D : a.dk, c0 = wv * 32;
+    const int dk = D >= 64 ? D : a.dk, c0 = (wv % NW) * 32;
     float *st = a.state + ((int64_t)req * a.n_chains + chain) * dk * dk;
-    const int e0 = a.list_off[req], m = a.list_off[req + 1] - e0;
+    const int len = a.list_off[req + 1] - a.list_off[req];
+    if (TREE && j0 >= len) return;  // uniform over the workgroup
+    // this workgroup's entries: e0 .. e0 + m - 1 (list positions j0 ..)
+    const int e0 = a.list_off[req] + j0;
+    const int m = TREE ? (len - j0 < t.B ? len - j0 : t.B) : len;
 
     // pair ids and seam starts of 64 entries at a time: lane l holds entry
     // base + l, read back with readlane (no dependent scalar loads per entry)
@@ -213,7 +234,18 @@ k_compose_dense(ComposeArgs a) {
     const bool seam_one_stage = !fam_vgate(FAM) && a.has_seam && a.w <= SEAM_STAGE;
 
     f32x4 X[RT][2];
-    load_tile<D>(X, st, dk, dk, c0, dk);
+    if (TREE) {
+        if (isS) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) X[rt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        } else {
+            identity_tile<D>(X, c0);
+        }
+    } else {
+        load_tile<D>(X, st, dk, dk, c0, dk);
+    }
     if (m > 0) {
         win_load(0);
         t_load(0);
@@ -237,12 +269,14 @@ k_compose_dense(ComposeArgs a) {
                     else
                         stage_seam<D, FAM, TIN>(sm, a.x, chain, dk, sb + s0, nt);
                     __syncthreads();
-                    float *o_first = a.o + (((int64_t)e * a.w + s0) * a.n_chains + chain) * dk;
+                    float *o_first =
+                        isS ? a.o + (((int64_t)e * a.w + s0) * a.n_chains + chain) * dk
+                            : t.pvec + ((((int64_t)req * t.max_list + j0 + j) * a.w + s0) * a.n_chains + chain) * dk;
                     if constexpr (CHUNK_SEAM)
                         seam_chunk_bf16<D, FAM>(X, sm, nt, o_first, (int64_t)a.n_chains * dk, c0, dk,
-                                                seam_nm[wv][0], seam_nm[wv][1]);
+                                                seam_nm[wv][0], seam_nm[wv][1], !isS);
                     else
-                        seam_tokens<D, FAM>(X, sm, nt, o_first, (int64_t)a.n_chains * dk, c0, c0, false, dk);
+                        seam_tokens<D, FAM>(X, sm, nt, o_first, (int64_t)a.n_chains * dk, c0, c0, !isS, dk);
                 }
             }
         }
@@ -257,7 +291,10 @@ k_compose_dense(ComposeArgs a) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) X[rt][nt] = quad_transpose(spre[rt][nt], lane);
+                for (int nt = 0; nt < 2; ++nt) {
+                    const f32x4 sj = quad_transpose(spre[rt][nt], lane);
+                    X[rt][nt] = isS ? sj : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
             // (past the last entry these re-read the last one: the same loads on
             // every path keep the compiler's wait counts exact)
             const int jn = j + 1 < m ? j + 1 : j;
@@ -286,7 +323,10 @@ k_compose_dense(ComposeArgs a) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) X[rt][nt] = quad_transpose(spre[rt][nt], lane);
+                for (int nt = 0; nt < 2; ++nt) {
+                    const f32x4 sj = quad_transpose(spre[rt][nt], lane);
+                    X[rt][nt] = isS ? sj : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
             const int jn = j + 1 < m ? j + 1 : j;
             s_load(jn);
             if (seam_one_stage) seam_fetch<D, FAM, TIN>(seam_pf, a.x, chain, dk, sb_at(jn), a.w);
@@ -310,7 +350,12 @@ k_compose_dense(ComposeArgs a) {
         t_load(j + 2 < m ? j + 2 : m - 1);
         __syncthreads();
     }
-    store_tile<D>(X, st, dk, dk, c0, dk);
+    if (TREE) {
+        const int64_t agg = (((int64_t)req * t.NB + blk) * a.n_chains + chain) * dk * dk;
+        store_tile<D>(X, (isS ? t.aggS : t.aggT) + agg, dk, dk, c0, dk);
+    } else {
+        store_tile<D>(X, st, dk, dk, c0, dk);
+    }
 }
 
 // ---- tree mode --------------------------------------------------------------
@@ -462,9 +507,11 @@ k_tree_fix(TreeArgs t) {
 template <int D, int FAM, typename TIN>
 static hipError_t launch_compose(const ComposeArgs &a, int n_req, hipStream_t st) {
     const dim3 grid((unsigned)(n_req * (int64_t)a.n_chains)), block(D / 32 * 64);
-    if constexpr (fam_dense(FAM))
-        hipLaunchKernelGGL((k_compose_dense<D, FAM, TIN>), grid, block, 0, st, a);
-    else
+    if constexpr (fam_dense(FAM)) {
+        TreeArgs t{};
+        t.c = a;
+        hipLaunchKernelGGL((k_compose_dense<D, FAM, TIN, false>), grid, block, 0, st, t);
+    } else
         hipLaunchKernelGGL((k_compose_seq<D, FAM, TIN>), grid, block, 0, st, a);
     return hipGetLastError();
 }
@@ -479,7 +526,10 @@ static hipError_t launch_seam(const SeamArgs &a, int n_items, hipStream_t st) {
 template <int D, int FAM, typename TIN>
 static hipError_t launch_tree(const TreeArgs &t, int n_req, hipStream_t st) {
     const unsigned blocks = (unsigned)((int64_t)n_req * t.NB * t.c.n_chains);
-    hipLaunchKernelGGL((k_tree_block<D, FAM, TIN>), dim3(blocks), dim3(2 * D / 32 * 64), 0, st, t);
+    if constexpr (fam_dense(FAM))
+        hipLaunchKernelGGL((k_compose_dense<D, FAM, TIN, true>), dim3(blocks), dim3(2 * D / 32 * 64), 0, st, t);
+    else
+        hipLaunchKernelGGL((k_tree_block<D, FAM, TIN>), dim3(blocks), dim3(2 * D / 32 * 64), 0, st, t);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((k_tree_scan<D, TIN>), dim3((unsigned)(n_req * (int64_t)t.c.n_chains)), dim3(D / 32 * 64), 0, st,

@@ -165,8 +165,8 @@ __device__ __forceinline__ f32x4 quad_transpose(f32x4 r, int lane) {
 }
 
 // One seam stage's tokens, fetched into registers ahead of use: thread tid
-// covers token tid / (D/4), features 4 (tid % (D/4)) .. +3 of q, k and v, and
-// (for the first feature quad) the token's gate and beta.
+// (tid < 2d) covers token tid / (D/4), features 4 (tid % (D/4)) .. +3 of q, k
+// and v, and (for the first feature quad) the token's gate and beta.
 template <int D, typename TIN>
 struct SeamPrefetch {
     using V4 = typename std::conditional<std::is_same<TIN, float>::value, f32x4, bf16x4>::type;
@@ -195,7 +195,9 @@ __device__ __forceinline__ TIN buffer_scalar(__amdgpu_buffer_rsrc_t r, int off) 
 template <int D, int FAM, typename TIN>
 __device__ __forceinline__ void seam_fetch(SeamPrefetch<D, TIN> &p, const Tok &x, int chain, int dk, int64_t tok0, int nt) {
     using V4 = typename SeamPrefetch<D, TIN>::V4;
-    const int tid = threadIdx.x, t = tid / (D / 4), i = 4 * (tid % (D / 4));
+    // threads past the stage's 2d items (workgroups wider than d/32 waves)
+    // repeat the first ones' loads and write nothing in seam_put
+    const int tid = threadIdx.x, t = (tid / (D / 4)) % SEAM_STAGE, i = 4 * (tid % (D / 4));
     const bool on = tok0 >= 0;
     const int64_t tb = on ? tok0 : 0;
     const int row_bytes = (int)(((int64_t)(nt - 1) * x.ts + dk) * sizeof(TIN));
@@ -227,6 +229,7 @@ __device__ __forceinline__ void seam_fetch(SeamPrefetch<D, TIN> &p, const Tok &x
 template <int D, int FAM, typename TIN>
 __device__ __forceinline__ void seam_put(SeamSmem<D, FAM> &sm, const SeamPrefetch<D, TIN> &p, int dk, int nt) {
     const int tid = threadIdx.x, t = tid / (D / 4), i = 4 * (tid % (D / 4));
+    if (t >= SEAM_STAGE) return;  // (wave-uniform: whole waves past the stage's items)
     const bool ok = t < nt && i < dk;
     f32x4 q4, k4, v4;
 #pragma unroll
@@ -277,10 +280,13 @@ __device__ __forceinline__ f32x4 mfma16(const s4v &a, const s4v &b, f32x4 c) {
 // which is the token recurrence S_t = a_t (I - beta_t k_t k_t^T) S_{t-1} +
 // beta_t k_t v_t^T, o_t = S_t^T q_t, regrouped.  Every decay factor is a
 // product of a's, so none exceeds 1.  Tokens past nt are zero tokens with
-// a = beta = 1.  sNw, sMw: this wave's 8 x 9 fp32 scratch.
+// a = beta = 1.  sNw, sMw: this wave's 8 x 9 fp32 scratch.  v_zero: the
+// tile's values are zero (the T half of a [T | S] pair), which makes the
+// read-out T^T q, the pulled-back query.
 template <int D, int FAM>
 __device__ void seam_chunk_bf16(f32x4 (&X)[D / 16][2], const SeamSmem<D, FAM> &sm, int nt, float *o_first,
-                                int64_t o_tok_stride, int c0, int dk, float (*sNw)[9], float (*sMw)[9]) {
+                                int64_t o_tok_stride, int c0, int dk, float (*sNw)[9], float (*sMw)[9],
+                                bool v_zero = false) {
     constexpr int RT = D / 16, KB = D / 32;
     const int lane = lane_id(), r16 = lane & 15, grp = lane >> 4;
     float a[SEAM_STAGE], eg[SEAM_STAGE], ec[SEAM_STAGE];
@@ -378,7 +384,7 @@ __device__ void seam_chunk_bf16(f32x4 (&X)[D / 16][2], const SeamSmem<D, FAM> &s
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int t = 4 * grp + jj;
-                yv[jj] = sm.v[t][col < D ? col : D - 1] - eg4[jj] * P[n2][jj];
+                yv[jj] = (v_zero ? 0.f : sm.v[t][col < D ? col : D - 1]) - eg4[jj] * P[n2][jj];
             }
         }
         s4v yh, yl;
