@@ -53,6 +53,16 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f3
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// The lane index as a value the compiler cannot carry across calls: per-lane
+// constants derived from it are recomputed where they are used instead of
+// being hoisted out of a loop, where they would hold registers for its whole
+// length (the empty asm emits no instruction).
+__device__ __forceinline__ int lane_fresh() {
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    return lane;
+}
+
 __device__ __forceinline__ void split1(float x, bf16 &h, bf16 &l) {
     h = (bf16)x;
     l = (bf16)(x - (float)h);

@@ -116,6 +116,26 @@ struct DenseTLds {
 // entries from (I, 0) on [T_p | S_p] with 2d/32 waves: the T half takes no
 // S_j and, at seams, zero values, so its seam read-out is the pulled-back
 // query T_p^T q_t; the block aggregate is written at the end.
+// Output rows of seam tokens s0 .. of list entry e: the S half writes o_t,
+// the T half of a tree block writes the pulled-back queries.
+__device__ __forceinline__ float *seam_out(const TreeArgs &t, bool isS, int e, int req, int jl, int chain, int s0,
+                                           int dk) {
+    const ComposeArgs &a = t.c;
+    return isS ? a.o + (((int64_t)e * a.w + s0) * a.n_chains + chain) * dk
+               : t.pvec + ((((int64_t)req * t.max_list + jl) * a.w + s0) * a.n_chains + chain) * dk;
+}
+
+// One staged stage of nt seam tokens on the wave's columns.
+template <int D, int FAM, bool CHUNK>
+__device__ __forceinline__ void seam_stage_run(f32x4 (&X)[D / 16][2], const SeamSmem<D, FAM> &sm, int nt,
+                                               float *o_first, const ComposeArgs &a, int c0, int dk,
+                                               float (*nm)[SEAM_STAGE][9], bool v_zero) {
+    if constexpr (CHUNK)
+        seam_chunk_bf16<D, FAM>(X, sm, nt, o_first, (int64_t)a.n_chains * dk, c0, dk, nm[0], nm[1], v_zero);
+    else
+        seam_tokens<D, FAM>(X, sm, nt, o_first, (int64_t)a.n_chains * dk, c0, c0, v_zero, dk);
+}
+
 template <int D, int FAM, typename TIN, bool TREE>
 __global__ void __launch_bounds__((TREE ? 2 : 1) * D / 32 * 64)
 k_compose_dense(TreeArgs t) {
@@ -260,23 +280,22 @@ k_compose_dense(TreeArgs t) {
         if (j + 2 >= win_base + 64) win_load(j);
         if (a.has_seam) {
             const int64_t sb = sb_at(j);
-            if (sb >= 0) {
+            if (sb >= 0 && seam_one_stage) {
+                // the whole window was fetched ahead: no loop around it, so the
+                // compiler's wait counts stay exact through this block
+                __syncthreads();
+                seam_put<D, FAM, TIN>(sm, seam_pf, dk, a.w);
+                __syncthreads();
+                seam_stage_run<D, FAM, CHUNK_SEAM>(X, sm, a.w, seam_out(t, isS, e, req, j0 + j, chain, 0, dk), a, c0,
+                                                   dk, seam_nm[wv], !isS);
+            } else if (sb >= 0) {
                 for (int s0 = 0; s0 < a.w; s0 += SEAM_STAGE) {
                     const int nt = a.w - s0 < SEAM_STAGE ? a.w - s0 : SEAM_STAGE;
                     __syncthreads();
-                    if (seam_one_stage)
-                        seam_put<D, FAM, TIN>(sm, seam_pf, dk, nt);
-                    else
-                        stage_seam<D, FAM, TIN>(sm, a.x, chain, dk, sb + s0, nt);
+                    stage_seam<D, FAM, TIN>(sm, a.x, chain, dk, sb + s0, nt);
                     __syncthreads();
-                    float *o_first =
-                        isS ? a.o + (((int64_t)e * a.w + s0) * a.n_chains + chain) * dk
-                            : t.pvec + ((((int64_t)req * t.max_list + j0 + j) * a.w + s0) * a.n_chains + chain) * dk;
-                    if constexpr (CHUNK_SEAM)
-                        seam_chunk_bf16<D, FAM>(X, sm, nt, o_first, (int64_t)a.n_chains * dk, c0, dk,
-                                                seam_nm[wv][0], seam_nm[wv][1], !isS);
-                    else
-                        seam_tokens<D, FAM>(X, sm, nt, o_first, (int64_t)a.n_chains * dk, c0, c0, !isS, dk);
+                    seam_stage_run<D, FAM, CHUNK_SEAM>(X, sm, nt, seam_out(t, isS, e, req, j0 + j, chain, s0, dk), a,
+                                                       c0, dk, seam_nm[wv], !isS);
                 }
             }
         }
@@ -356,6 +375,192 @@ k_compose_dense(TreeArgs t) {
     } else {
         store_tile<D>(X, st, dk, dk, c0, dk);
     }
+}
+
+// Sequential compose, lean form, for bf16 inputs of the scalar-gate erasing
+// families (DeltaNet, GDN) at d >= 64: the same product and seam chunk as
+// k_compose_dense, laid out so that two workgroups share a compute unit and
+// hide each other's waits.  One LDS copy of T (hi | lo bf16 rows) and bf16
+// seam staging keep a workgroup's LDS under half of the compute unit's; at most
+// 256 registers per lane.  Per entry j:
+//   seam:    the prefetched window of entry j is staged and the state advanced
+//            through it (chunk form on the matrix cores);
+//   product: the state becomes the B operand, the accumulators take S_j
+//            (loaded during the previous staging phase), the next window is
+//            fetched, then S <- T_j S + S_j from the LDS copy;
+//   staging: once every wave is past the product, T_{j+1} and S_{j+1} are
+//            requested and T_{j+1} is written into the LDS copy (the wait for
+//            it is the other workgroup's time on the compute unit).
+template <int D, int FAM>
+__global__ void __launch_bounds__(D / 32 * 64, 2)
+k_compose_lean(ComposeArgs a) {
+    static_assert(D >= 64 && (FAM == DELTANET || FAM == GDN), "lean compose: d >= 64, scalar-gate erasing families");
+    constexpr int NW = D / 32, RT = D / 16, KB = D / 32;
+    using TL = DenseTLds<D, false>;
+    constexpr int LDT = TL::LDT;
+    constexpr int NV = D * D / 4 / 64 / NW;  // 16-byte pieces of T per lane
+    constexpr int RPW = D / NW;              // T rows staged by one wave
+    constexpr int dk = D;
+    __shared__ __attribute__((aligned(16))) bf16 tsm[D * LDT];
+    __shared__ SeamSmemB<D> sm;
+    __shared__ float seam_nm[NW][2][SEAM_STAGE][9];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int r16 = lane & 15, grp = lane >> 4;
+    const int req = blockIdx.x / a.n_chains, chain = blockIdx.x % a.n_chains;
+    const int c0 = wv * 32;
+    float *st = a.state + ((int64_t)req * a.n_chains + chain) * dk * dk;
+    const int e0 = a.list_off[req];
+    const int m = a.list_off[req + 1] - e0;
+
+    // pair ids and seam starts of 64 entries at a time, read back with readlane
+    int win_base = 0, win_pid = 0;
+    int64_t win_sb = -1;
+    auto win_load = [&](int b) {
+        win_base = b;
+        const int idx = b + lane < m ? b + lane : m - 1;
+        win_pid = a.pair_id[e0 + idx];
+        win_sb = a.has_seam ? a.seam_begin[e0 + idx] : -1;
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): settled here, not at every later use
+    };
+    auto pid_at = [&](int j) -> int64_t { return __builtin_amdgcn_readlane(win_pid, j - win_base); };
+    auto sb_at = [&](int j) -> int64_t {
+        const uint64_t u = (uint64_t)win_sb;
+        const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, j - win_base);
+        const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), j - win_base);
+        return (int64_t)(((uint64_t)hi << 32) | lo);
+    };
+
+    f32x4 tpre[NV];
+    f32x4 spre[RT][2];
+    auto t_load = [&](int j, int ln) {
+        const float *Tp = a.T + (pid_at(j) * a.n_chains + chain) * a.t_elems;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int item = i * 64 + ln, row = wv * RPW + item / (D / 4), c4 = item % (D / 4);
+            tpre[i] = *reinterpret_cast<const f32x4 *>(Tp + row * D + 4 * c4);
+        }
+    };
+    auto t_put = [&](int ln) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int item = i * 64 + ln, row = wv * RPW + item / (D / 4), c4 = item % (D / 4);
+            // columns permuted within each 32-block so that a lane's A fragment
+            // (k = 4grp.., 16+4grp..) is 8 consecutive bf16
+            const int sub = c4 % 8, pos = 32 * (c4 / 8) + 8 * (sub % 4) + 4 * (sub / 4);
+            bf16x4 h, l;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                h[e] = (bf16)tpre[i][e];
+                l[e] = (bf16)(tpre[i][e] - (float)h[e]);
+            }
+            bf16 *tr = tsm + row * LDT;
+            *reinterpret_cast<bf16x4 *>(tr + pos) = h;
+            *reinterpret_cast<bf16x4 *>(tr + D + pos) = l;
+        }
+    };
+    // a d x d row-major matrix's columns c0 .. c0+31 in row quads: lane
+    // (4q + i, grp) takes row 4 grp + i, columns 4q .. 4q+3 of each tile (one
+    // quad transpose from the C layout)
+    auto s_load = [&](int j, int ln) {
+        const int rw = 4 * (ln >> 4) + (ln & 3), cl = c0 + 4 * ((ln & 15) >> 2);
+        const float *Sp = a.S + (pid_at(j) * a.n_chains + chain) * dk * dk;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+                spre[rt][nt] = *reinterpret_cast<const f32x4 *>(Sp + (16 * rt + rw) * D + cl + 16 * nt);
+    };
+    SeamPrefetch<D, bf16> seam_pf;
+    const bool seam_one_stage = a.has_seam && a.w <= SEAM_STAGE;
+
+    f32x4 X[RT][2];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+            X[rt][nt] = quad_transpose(
+                *reinterpret_cast<const f32x4 *>(st + (16 * rt + 4 * grp + (r16 & 3)) * D + c0 + 4 * (r16 >> 2) + 16 * nt),
+                lane);
+    if (m > 0) {
+        win_load(0);
+        t_load(0, lane);
+        s_load(0, lane);
+        if (seam_one_stage) seam_fetch<D, FAM, bf16>(seam_pf, a.x, chain, dk, sb_at(0), a.w);
+        t_put(lane);
+        __syncthreads();
+    }
+    for (int j = 0; j < m; ++j) {
+        const int e = e0 + j;
+        if (j + 2 >= win_base + 64) win_load(j);
+        const int ln = lane_fresh(), lr16 = ln & 15, lgrp = ln >> 4;
+        if (a.has_seam) {
+            const int64_t sb = sb_at(j);
+            float *o_first = a.o + ((int64_t)e * a.w * a.n_chains + chain) * dk;
+            if (sb >= 0 && seam_one_stage) {
+                // the staging area's last readers finished before the barrier
+                // that closed the previous entry
+                seam_put_b<D, FAM>(sm, seam_pf, a.w);
+                __syncthreads();
+                seam_chunk_bf16<D, FAM>(X, sm, a.w, o_first, (int64_t)a.n_chains * dk, c0, dk, seam_nm[wv][0],
+                                        seam_nm[wv][1]);
+            } else if (sb >= 0) {
+                for (int s0 = 0; s0 < a.w; s0 += SEAM_STAGE) {
+                    const int nt = a.w - s0 < SEAM_STAGE ? a.w - s0 : SEAM_STAGE;
+                    __syncthreads();
+                    stage_seam_b<D, FAM>(sm, a.x, chain, sb + s0, nt);
+                    __syncthreads();
+                    seam_chunk_bf16<D, FAM>(X, sm, nt, o_first + (int64_t)s0 * a.n_chains * dk,
+                                            (int64_t)a.n_chains * dk, c0, dk, seam_nm[wv][0], seam_nm[wv][1]);
+                }
+            }
+        }
+        // S <- T_j S + S_j
+        bf16x8 xh[KB][2], xl[KB][2];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                float xv[8];
+                acc_to_perm(X[2 * kb][nt], X[2 * kb + 1][nt], xv);
+                split8(xv, xh[kb][nt], xl[kb][nt]);
+            }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) X[rt][nt] = quad_transpose(spre[rt][nt], ln);
+        // (past the last entry these re-read the last one: the same loads on
+        // every path keep the compiler's wait counts exact)
+        const int jn = j + 1 < m ? j + 1 : j;
+        if (seam_one_stage) seam_fetch<D, FAM, bf16>(seam_pf, a.x, chain, dk, sb_at(jn), a.w);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int off = (16 * rt + lr16) * LDT + 32 * kb + 8 * lgrp;
+                const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(tsm + off);
+                const bf16x8 al = *reinterpret_cast<const bf16x8 *>(tsm + D + off);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    X[rt][nt] = mfma(ah, xh[kb][nt], X[rt][nt]);
+                    X[rt][nt] = mfma(ah, xl[kb][nt], X[rt][nt]);
+                    X[rt][nt] = mfma(al, xh[kb][nt], X[rt][nt]);
+                }
+            }
+        __syncthreads();  // every wave is past T_j and the seam staging
+        const int ln2 = lane_fresh();
+        t_load(jn, ln2);
+        s_load(jn, ln2);
+        t_put(ln2);
+        __syncthreads();  // T_{j+1} in place
+    }
+    // (the row-quad store, so that no per-element address outlives the loop)
+    const int lane2 = lane_fresh();
+    const int rw2 = 4 * ((lane2 >> 4) & 3) + (lane2 & 3), cl2 = c0 + 4 * ((lane2 & 15) >> 2);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+            *reinterpret_cast<f32x4 *>(st + (16 * rt + rw2) * D + cl2 + 16 * nt) = quad_transpose(X[rt][nt], lane);
 }
 
 // ---- tree mode --------------------------------------------------------------
@@ -507,7 +712,9 @@ k_tree_fix(TreeArgs t) {
 template <int D, int FAM, typename TIN>
 static hipError_t launch_compose(const ComposeArgs &a, int n_req, hipStream_t st) {
     const dim3 grid((unsigned)(n_req * (int64_t)a.n_chains)), block(D / 32 * 64);
-    if constexpr (fam_dense(FAM)) {
+    if constexpr (std::is_same<TIN, bf16>::value && D >= 64 && (FAM == DELTANET || FAM == GDN)) {
+        hipLaunchKernelGGL((k_compose_lean<D, FAM>), grid, block, 0, st, a);
+    } else if constexpr (fam_dense(FAM)) {
         TreeArgs t{};
         t.c = a;
         hipLaunchKernelGGL((k_compose_dense<D, FAM, TIN, false>), grid, block, 0, st, t);

@@ -25,6 +25,45 @@ struct SeamSmem {
     float beta[SEAM_STAGE];
 };
 
+// The same stage with q, k, v kept as bf16 (bf16 inputs, scalar gates): half
+// the LDS, and the rows are matrix-core operands as they stand.
+template <int D>
+struct SeamSmemB {
+    bf16 q[SEAM_STAGE][D];
+    bf16 k[SEAM_STAGE][D];
+    bf16 v[SEAM_STAGE][D];
+    float a[SEAM_STAGE][1];
+    float beta[SEAM_STAGE];
+};
+
+// Stage tokens tok0 .. tok0+nt-1 of `chain` into bf16 rows (scalar-gate
+// families; rows past nt are zero tokens with a = beta = 1).
+template <int D, int FAM>
+__device__ void stage_seam_b(SeamSmemB<D> &sm, const Tok &x, int chain, int64_t tok0, int nt) {
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const bf16 *qp = reinterpret_cast<const bf16 *>(x.q) + (int64_t)chain * x.cs;
+    const bf16 *kp = reinterpret_cast<const bf16 *>(x.k) + (int64_t)chain * x.cs;
+    const bf16 *vp = reinterpret_cast<const bf16 *>(x.v) + (int64_t)chain * x.cs;
+    for (int item = tid; item < SEAM_STAGE * D; item += nthr) {
+        const int t = item / D, i = item % D;
+        const bool ok = t < nt;
+        const int64_t off = (tok0 + (ok ? t : nt - 1)) * x.ts + i;
+        const bf16 qv = qp[off], kv = kp[off], vv = vp[off];
+        sm.q[t][i] = ok ? qv : (bf16)0.f;
+        sm.k[t][i] = ok ? kv : (bf16)0.f;
+        sm.v[t][i] = ok ? vv : (bf16)0.f;
+    }
+    if (tid < SEAM_STAGE) {
+        const int t = tid;
+        const int64_t tc = tok0 + (t < nt ? t : nt - 1);
+        float av = 1.f, bv = 1.f;
+        if (fam_sgate(FAM)) av = expf(ldf(reinterpret_cast<const bf16 *>(x.g) + (int64_t)chain * x.gcs + tc * x.gts));
+        if (fam_beta(FAM)) bv = ldf(reinterpret_cast<const bf16 *>(x.beta) + (int64_t)chain * x.bcs + tc * x.bts);
+        sm.a[t][0] = t < nt ? av : 1.f;
+        sm.beta[t] = t < nt ? bv : 1.f;
+    }
+}
+
 // Stage tokens tok0 .. tok0+nt-1 of `chain` (rows past nt are zero tokens).
 template <int D, int FAM, typename TIN>
 __device__ void stage_seam(SeamSmem<D, FAM> &sm, const Tok &x, int chain, int dk, int64_t tok0, int nt) {
@@ -171,7 +210,10 @@ template <int D, typename TIN>
 struct SeamPrefetch {
     using V4 = typename std::conditional<std::is_same<TIN, float>::value, f32x4, bf16x4>::type;
     V4 q, k, v;
-    TIN g, b;
+    // gate and beta as raw bits in full registers (a bf16 sits in the low
+    // half): 16-bit values packed into one register would be combined right
+    // after the load, which waits for every load issued before them
+    uint32_t g, b;
 };
 
 // A raw buffer view of nbytes from p (p wave-uniform); reads past nbytes return
@@ -181,11 +223,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const void *p, int
 }
 
 template <typename TIN>
-__device__ __forceinline__ TIN buffer_scalar(__amdgpu_buffer_rsrc_t r, int off) {
+__device__ __forceinline__ uint32_t buffer_scalar_bits(__amdgpu_buffer_rsrc_t r, int off) {
     if constexpr (std::is_same<TIN, float>::value)
-        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+        return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
     else
-        return __builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+        return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+template <typename TIN>
+__device__ __forceinline__ float scalar_from_bits(uint32_t u) {
+    if constexpr (std::is_same<TIN, float>::value)
+        return __builtin_bit_cast(float, u);
+    else
+        return __builtin_bit_cast(float, u << 16);
 }
 
 // Fetch the seam stage of tokens tok0 .. tok0 + nt - 1 of `chain`; when the
@@ -216,12 +266,12 @@ __device__ __forceinline__ void seam_fetch(SeamPrefetch<D, TIN> &p, const Tok &x
     if (fam_sgate(FAM)) {
         const auto r = buffer_view(reinterpret_cast<const TIN *>(x.g) + (int64_t)chain * x.gcs + tb * x.gts,
                                    on ? (int)(((int64_t)(nt - 1) * x.gts + 1) * sizeof(TIN)) : 0);
-        p.g = buffer_scalar<TIN>(r, (int)((int64_t)t * x.gts * sizeof(TIN)));
+        p.g = buffer_scalar_bits<TIN>(r, (int)((int64_t)t * x.gts * sizeof(TIN)));
     }
     if (fam_beta(FAM)) {
         const auto r = buffer_view(reinterpret_cast<const TIN *>(x.beta) + (int64_t)chain * x.bcs + tb * x.bts,
                                    on ? (int)(((int64_t)(nt - 1) * x.bts + 1) * sizeof(TIN)) : 0);
-        p.b = buffer_scalar<TIN>(r, (int)((int64_t)t * x.bts * sizeof(TIN)));
+        p.b = buffer_scalar_bits<TIN>(r, (int)((int64_t)t * x.bts * sizeof(TIN)));
     }
 }
 
@@ -242,8 +292,24 @@ __device__ __forceinline__ void seam_put(SeamSmem<D, FAM> &sm, const SeamPrefetc
     *reinterpret_cast<f32x4 *>(&sm.k[t][i]) = k4;
     *reinterpret_cast<f32x4 *>(&sm.v[t][i]) = v4;
     if (i == 0) {
-        sm.a[t][0] = (fam_sgate(FAM) && t < nt) ? expf((float)p.g) : 1.f;
-        sm.beta[t] = (fam_beta(FAM) && t < nt) ? (float)p.b : 1.f;
+        sm.a[t][0] = (fam_sgate(FAM) && t < nt) ? expf(scalar_from_bits<TIN>(p.g)) : 1.f;
+        sm.beta[t] = (fam_beta(FAM) && t < nt) ? scalar_from_bits<TIN>(p.b) : 1.f;
+    }
+}
+
+// Write a fetched stage (bf16 inputs) into bf16 staging rows.
+template <int D, int FAM>
+__device__ __forceinline__ void seam_put_b(SeamSmemB<D> &sm, const SeamPrefetch<D, bf16> &p, int nt) {
+    const int tid = threadIdx.x, t = tid / (D / 4), i = 4 * (tid % (D / 4));
+    if (t >= SEAM_STAGE) return;  // (wave-uniform: whole waves past the stage's items)
+    const bool ok = t < nt;
+    const bf16x4 z = {(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    *reinterpret_cast<bf16x4 *>(&sm.q[t][i]) = ok ? p.q : z;
+    *reinterpret_cast<bf16x4 *>(&sm.k[t][i]) = ok ? p.k : z;
+    *reinterpret_cast<bf16x4 *>(&sm.v[t][i]) = ok ? p.v : z;
+    if (i == 0) {
+        sm.a[t][0] = (fam_sgate(FAM) && ok) ? expf(scalar_from_bits<bf16>(p.g)) : 1.f;
+        sm.beta[t] = (fam_beta(FAM) && ok) ? scalar_from_bits<bf16>(p.b) : 1.f;
     }
 }
 
@@ -283,12 +349,12 @@ __device__ __forceinline__ f32x4 mfma16(const s4v &a, const s4v &b, f32x4 c) {
 // a = beta = 1.  sNw, sMw: this wave's 8 x 9 fp32 scratch.  v_zero: the
 // tile's values are zero (the T half of a [T | S] pair), which makes the
 // read-out T^T q, the pulled-back query.
-template <int D, int FAM>
-__device__ void seam_chunk_bf16(f32x4 (&X)[D / 16][2], const SeamSmem<D, FAM> &sm, int nt, float *o_first,
+template <int D, int FAM, typename SM>
+__device__ void seam_chunk_bf16(f32x4 (&X)[D / 16][2], const SM &sm, int nt, float *o_first,
                                 int64_t o_tok_stride, int c0, int dk, float (*sNw)[9], float (*sMw)[9],
                                 bool v_zero = false) {
     constexpr int RT = D / 16, KB = D / 32;
-    const int lane = lane_id(), r16 = lane & 15, grp = lane >> 4;
+    const int lane = lane_fresh(), r16 = lane & 15, grp = lane >> 4;
     float a[SEAM_STAGE], eg[SEAM_STAGE], ec[SEAM_STAGE];
 #pragma unroll
     for (int t = 0; t < SEAM_STAGE; ++t) a[t] = FAM == GDN ? sm.a[t][0] : 1.f;
@@ -305,18 +371,24 @@ __device__ void seam_chunk_bf16(f32x4 (&X)[D / 16][2], const SeamSmem<D, FAM> &s
     }
     const float lam = eg[SEAM_STAGE - 1];
     // P = [K; Q] S0 (rows 0-7: K S0, rows 8-15: Q S0) and the Gram [K;Q][K;Q]^T
-    const float *qk = r16 < 8 ? &sm.k[r16][0] : &sm.q[r16 - 8][0];
+    using E = typename std::remove_cv<typename std::remove_reference<decltype(sm.k[0][0])>::type>::type;
+    constexpr bool B16 = std::is_same<E, bf16>::value;
+    const E *qk = r16 < 8 ? &sm.k[r16][0] : &sm.q[r16 - 8][0];
     f32x4 P[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     f32x4 G = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-        const f32x4 u = *reinterpret_cast<const f32x4 *>(qk + 32 * kb + 4 * grp);
-        const f32x4 w = *reinterpret_cast<const f32x4 *>(qk + 32 * kb + 16 + 4 * grp);
         bf16x8 af;
+        if constexpr (B16) {
+            af = lds_perm(qk, 0, 0, 32 * kb, grp);
+        } else {
+            const f32x4 u = *reinterpret_cast<const f32x4 *>(qk + 32 * kb + 4 * grp);
+            const f32x4 w = *reinterpret_cast<const f32x4 *>(qk + 32 * kb + 16 + 4 * grp);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            af[e] = (bf16)u[e];
-            af[4 + e] = (bf16)w[e];
+            for (int e = 0; e < 4; ++e) {
+                af[e] = (bf16)u[e];
+                af[4 + e] = (bf16)w[e];
+            }
         }
         G = mfma(af, af, G);
 #pragma unroll
@@ -384,7 +456,7 @@ __device__ void seam_chunk_bf16(f32x4 (&X)[D / 16][2], const SeamSmem<D, FAM> &s
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int t = 4 * grp + jj;
-                yv[jj] = (v_zero ? 0.f : sm.v[t][col < D ? col : D - 1]) - eg4[jj] * P[n2][jj];
+                yv[jj] = (v_zero ? 0.f : (float)sm.v[t][col < D ? col : D - 1]) - eg4[jj] * P[n2][jj];
             }
         }
         s4v yh, yl;
@@ -417,9 +489,16 @@ __device__ void seam_chunk_bf16(f32x4 (&X)[D / 16][2], const SeamSmem<D, FAM> &s
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             s4v kt = {0, 0, 0, 0};
-            if (grp < 2)
-                kt = bf4(sm.k[4 * grp][16 * rt + r16], sm.k[4 * grp + 1][16 * rt + r16], sm.k[4 * grp + 2][16 * rt + r16],
-                         sm.k[4 * grp + 3][16 * rt + r16]);
+            if (grp < 2) {
+                if constexpr (B16)
+                    kt = s4v{__builtin_bit_cast(short, sm.k[4 * grp][16 * rt + r16]),
+                             __builtin_bit_cast(short, sm.k[4 * grp + 1][16 * rt + r16]),
+                             __builtin_bit_cast(short, sm.k[4 * grp + 2][16 * rt + r16]),
+                             __builtin_bit_cast(short, sm.k[4 * grp + 3][16 * rt + r16])};
+                else
+                    kt = bf4(sm.k[4 * grp][16 * rt + r16], sm.k[4 * grp + 1][16 * rt + r16],
+                             sm.k[4 * grp + 2][16 * rt + r16], sm.k[4 * grp + 3][16 * rt + r16]);
+            }
             f32x4 acc = X[rt][n2] * lam;
             acc = mfma16(kt, rh, acc);
             X[rt][n2] = mfma16(kt, rl, acc);
