@@ -68,14 +68,33 @@ __device__ __forceinline__ void split1(float x, bf16 &h, bf16 &l) {
     l = (bf16)(x - (float)h);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Split two fp32 values into hi = bf16(x) and lo = bf16(x - hi) (both round to
+// nearest even), as packed pairs: one packed conversion each, hi widened back
+// with a shift and a mask rather than converted again.
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t &h, uint32_t &l) {
+    h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+    const float h0 = __builtin_bit_cast(float, h << 16), h1 = __builtin_bit_cast(float, h & 0xffff0000u);
+    l = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0 - h0, x1 - h1}, bf16x2));
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 // Split eight fp32 values into hi / lo bf16 vectors.
 __device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &h, bf16x8 &l) {
+    u32x4 hu, lu;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        bf16 hh = (bf16)x[e];
-        h[e] = hh;
-        l[e] = (bf16)(x[e] - (float)hh);
+    for (int e = 0; e < 4; ++e) {
+        uint32_t a, b;
+        split2(x[2 * e], x[2 * e + 1], a, b);
+        hu[e] = a;
+        lu[e] = b;
     }
+    h = __builtin_bit_cast(bf16x8, hu);
+    l = __builtin_bit_cast(bf16x8, lu);
 }
 
 // 8 bf16 of row `row` of a row-major LDS matrix, permuted k subset at kbase.

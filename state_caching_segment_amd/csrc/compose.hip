@@ -430,57 +430,64 @@ k_compose_lean(ComposeArgs a) {
         return (int64_t)(((uint64_t)hi << 32) | lo);
     };
 
+    // Loads go through buffer views of the slot's T and S: one per-lane
+    // offset, the rest compile-time immediates (no per-load address math).
+    // T: lane ln of wave wv stages rows wv*RPW + i*(256/D) + ln/(D/4), columns
+    // 4 (ln % (D/4)) .. +3, for i < NV.
+    constexpr int TROWS = 256 / D;  // rows of T per 64-lane piece
     f32x4 tpre[NV];
-    f32x4 spre[RT][2];
     auto t_load = [&](int j, int ln) {
-        const float *Tp = a.T + (pid_at(j) * a.n_chains + chain) * a.t_elems;
+        const auto r = buffer_view(a.T + (pid_at(j) * a.n_chains + chain) * a.t_elems, D * D * 4);
+        const int voff = ((wv * RPW + (int)((unsigned)ln / (D / 4))) * D + 4 * (int)((unsigned)ln % (D / 4))) * 4;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int item = i * 64 + ln, row = wv * RPW + item / (D / 4), c4 = item % (D / 4);
-            tpre[i] = *reinterpret_cast<const f32x4 *>(Tp + row * D + 4 * c4);
-        }
+        for (int i = 0; i < NV; ++i)
+            tpre[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, i * TROWS * D * 4, 0));
     };
     auto t_put = [&](int ln) {
+        // columns permuted within each 32-block so that a lane's A fragment
+        // (k = 4grp.., 16+4grp..) is 8 consecutive bf16
+        const int c4 = (int)((unsigned)ln % (D / 4)), sub = c4 % 8;
+        const int pos = 32 * (c4 / 8) + 8 * (sub % 4) + 4 * (sub / 4);
+        bf16 *tr = tsm + (wv * RPW + (int)((unsigned)ln / (D / 4))) * LDT + pos;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int item = i * 64 + ln, row = wv * RPW + item / (D / 4), c4 = item % (D / 4);
-            // columns permuted within each 32-block so that a lane's A fragment
-            // (k = 4grp.., 16+4grp..) is 8 consecutive bf16
-            const int sub = c4 % 8, pos = 32 * (c4 / 8) + 8 * (sub % 4) + 4 * (sub / 4);
-            bf16x4 h, l;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                h[e] = (bf16)tpre[i][e];
-                l[e] = (bf16)(tpre[i][e] - (float)h[e]);
-            }
-            bf16 *tr = tsm + row * LDT;
-            *reinterpret_cast<bf16x4 *>(tr + pos) = h;
-            *reinterpret_cast<bf16x4 *>(tr + D + pos) = l;
+            uint32_t h0, l0, h1, l1;
+            split2(tpre[i][0], tpre[i][1], h0, l0);
+            split2(tpre[i][2], tpre[i][3], h1, l1);
+            *reinterpret_cast<u32x2 *>(tr + i * TROWS * LDT) = u32x2{h0, h1};
+            *reinterpret_cast<u32x2 *>(tr + i * TROWS * LDT + D) = u32x2{l0, l1};
         }
     };
-    // a d x d row-major matrix's columns c0 .. c0+31 in row quads: lane
-    // (4q + i, grp) takes row 4 grp + i, columns 4q .. 4q+3 of each tile (one
-    // quad transpose from the C layout)
+    // S_j straight into the C layout: spre[rt][nt][jj] = S_j[16 rt + 4 grp + jj][c0 + 16 nt + r16]
+    float spre[RT][2][4];
     auto s_load = [&](int j, int ln) {
-        const int rw = 4 * (ln >> 4) + (ln & 3), cl = c0 + 4 * ((ln & 15) >> 2);
-        const float *Sp = a.S + (pid_at(j) * a.n_chains + chain) * dk * dk;
+        const auto r = buffer_view(a.S + (pid_at(j) * a.n_chains + chain) * dk * dk, D * D * 4);
+        const int voff = ((int)((unsigned)ln >> 4) * 4 * D + c0 + (int)((unsigned)ln & 15)) * 4;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)
-                spre[rt][nt] = *reinterpret_cast<const f32x4 *>(Sp + (16 * rt + rw) * D + cl + 16 * nt);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    spre[rt][nt][jj] = __builtin_bit_cast(
+                        float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, ((16 * rt + jj) * D + 16 * nt) * 4, 0));
     };
     SeamPrefetch<D, bf16> seam_pf;
     const bool seam_one_stage = a.has_seam && a.w <= SEAM_STAGE;
 
     f32x4 X[RT][2];
+    {
+        const auto r = buffer_view(st, D * D * 4);
+        const int voff = (grp * 4 * D + c0 + r16) * 4;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-            X[rt][nt] = quad_transpose(
-                *reinterpret_cast<const f32x4 *>(st + (16 * rt + 4 * grp + (r16 & 3)) * D + c0 + 4 * (r16 >> 2) + 16 * nt),
-                lane);
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    X[rt][nt][jj] = __builtin_bit_cast(
+                        float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, ((16 * rt + jj) * D + 16 * nt) * 4, 0));
+    }
     if (m > 0) {
         win_load(0);
         t_load(0, lane);
@@ -527,7 +534,7 @@ k_compose_lean(ComposeArgs a) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) X[rt][nt] = quad_transpose(spre[rt][nt], ln);
+            for (int nt = 0; nt < 2; ++nt) X[rt][nt] = f32x4{spre[rt][nt][0], spre[rt][nt][1], spre[rt][nt][2], spre[rt][nt][3]};
         // (past the last entry these re-read the last one: the same loads on
         // every path keep the compiler's wait counts exact)
         const int jn = j + 1 < m ? j + 1 : j;
@@ -553,14 +560,23 @@ k_compose_lean(ComposeArgs a) {
         t_put(ln2);
         __syncthreads();  // T_{j+1} in place
     }
-    // (the row-quad store, so that no per-element address outlives the loop)
-    const int lane2 = lane_fresh();
-    const int rw2 = 4 * ((lane2 >> 4) & 3) + (lane2 & 3), cl2 = c0 + 4 * ((lane2 & 15) >> 2);
+    {
+        const int ln = lane_fresh();
+        const auto r = buffer_view(st, D * D * 4);
+        const int voff = ((int)((unsigned)ln >> 4) * 4 * D + c0 + (int)((unsigned)ln & 15)) * 4;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-            *reinterpret_cast<f32x4 *>(st + (16 * rt + rw2) * D + cl2 + 16 * nt) = quad_transpose(X[rt][nt], lane);
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    // (the element is copied out first: this compiler's
+                    // __builtin_bit_cast of a vector element reads element 0)
+                    const float v = X[rt][nt][jj];
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff,
+                                                          ((16 * rt + jj) * D + 16 * nt) * 4, 0);
+                }
+    }
 }
 
 // ---- tree mode --------------------------------------------------------------

@@ -321,12 +321,16 @@ __device__ __forceinline__ s4v bf4(float a, float b, float c, float d) {
 }
 
 __device__ __forceinline__ void split4v(const f32x4 &x, s4v &h, s4v &l) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const bf16 y = (bf16)x[e];
-        h[e] = __builtin_bit_cast(short, y);
-        l[e] = __builtin_bit_cast(short, (bf16)(x[e] - (float)y));
-    }
+    u32x2 hu, lu;
+    uint32_t a, b;
+    split2(x[0], x[1], a, b);
+    hu[0] = a;
+    lu[0] = b;
+    split2(x[2], x[3], a, b);
+    hu[1] = a;
+    lu[1] = b;
+    h = __builtin_bit_cast(s4v, hu);
+    l = __builtin_bit_cast(s4v, lu);
 }
 
 __device__ __forceinline__ f32x4 mfma16(const s4v &a, const s4v &b, f32x4 c) {
