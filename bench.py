@@ -101,10 +101,12 @@ def build_kernel(family, dtype):
     return "k_build_diag", ["build_diag.hip", "common.h"]
 
 
-def compose_kernel(family):
+def compose_kernel(family, in_bf16=True, d=128):
     """The sequential compose kernel the library dispatches for a family, and
     the sources whose hash keys its stored counter readings."""
     files = ["compose.hip", "compose_common.h", "common.h"]
+    if family in ("deltanet", "gdn") and in_bf16 and d >= 64:
+        return "k_compose_lean", files
     return ("k_compose_dense" if family in ("deltanet", "gdn", "kda") else "k_compose_seq"), files
 
 
@@ -291,7 +293,9 @@ def main():
     roof_build.update({"traffic": measured_traffic("build" + key, bk_files),
                        "kernel": bk_name, "alg_bytes": bb, "alg_flops": bf,
                        "mfma_frac_alg": b_mfma / BF16_PEAK, "hbm_frac_alg": b_hbm / HBM_PEAK})
-    ck_name, ck_files = compose_kernel(wl.family)
+    ck_name, ck_files = compose_kernel(wl.family, wl.dtype == "bf16", d)
+    if mode == hy.TREE:
+        ck_name = "k_compose_dense (tree block phase) + k_tree_scan + k_tree_fix"
     roof_comp = {"bound": "hbm", "achieved": cb / tc / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                  "frac": cb / tc / HBM_PEAK, "traffic": measured_traffic("compose" + key, ck_files),
                  "kernel": ck_name, "alg_bytes": cb,
