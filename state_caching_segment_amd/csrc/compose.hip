@@ -383,14 +383,16 @@ k_compose_dense(TreeArgs t) {
 // hide each other's waits.  One LDS copy of T (hi | lo bf16 rows) and bf16
 // seam staging keep a workgroup's LDS under half of the compute unit's; at most
 // 256 registers per lane.  Per entry j:
-//   seam:    the prefetched window of entry j is staged and the state advanced
-//            through it (chunk form on the matrix cores);
+//   seam:    the state is advanced through entry j's window, staged in LDS
+//            during the previous staging phase (chunk form on the matrix
+//            cores);
 //   product: the state becomes the B operand, the accumulators take S_j
-//            (loaded during the previous staging phase), the next window is
-//            fetched, then S <- T_j S + S_j from the LDS copy;
-//   staging: once every wave is past the product, T_{j+1} and S_{j+1} are
-//            requested and T_{j+1} is written into the LDS copy (the wait for
-//            it is the other workgroup's time on the compute unit).
+//            (loaded during the previous staging phase), then S <- T_j S + S_j
+//            from the LDS copy;
+//   staging: once every wave is past the product, the next window and
+//            T_{j+1} are requested and written into LDS (the wait for them is
+//            the other workgroup's time on the compute unit), then S_{j+1}
+//            requested.
 template <int D, int FAM>
 __global__ void __launch_bounds__(D / 32 * 64, 2)
 k_compose_lean(ComposeArgs a) {
@@ -490,9 +492,9 @@ k_compose_lean(ComposeArgs a) {
     }
     if (m > 0) {
         win_load(0);
-        t_load(0, lane);
-        s_load(0, lane);
         if (seam_one_stage) seam_fetch<D, FAM, bf16>(seam_pf, a.x, chain, dk, sb_at(0), a.w);
+        t_load(0, lane);
+        if (seam_one_stage) seam_put_b<D, FAM>(sm, seam_pf, a.w);
         t_put(lane);
         __syncthreads();
     }
@@ -504,10 +506,7 @@ k_compose_lean(ComposeArgs a) {
             const int64_t sb = sb_at(j);
             float *o_first = a.o + ((int64_t)e * a.w * a.n_chains + chain) * dk;
             if (sb >= 0 && seam_one_stage) {
-                // the staging area's last readers finished before the barrier
-                // that closed the previous entry
-                seam_put_b<D, FAM>(sm, seam_pf, a.w);
-                __syncthreads();
+                // (staged during the previous staging phase)
                 seam_chunk_bf16<D, FAM>(X, sm, a.w, o_first, (int64_t)a.n_chains * dk, c0, dk, seam_nm[wv][0],
                                         seam_nm[wv][1]);
             } else if (sb >= 0) {
@@ -531,14 +530,14 @@ k_compose_lean(ComposeArgs a) {
                 acc_to_perm(X[2 * kb][nt], X[2 * kb + 1][nt], xv);
                 split8(xv, xh[kb][nt], xl[kb][nt]);
             }
+        s_load(j, ln);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) X[rt][nt] = f32x4{spre[rt][nt][0], spre[rt][nt][1], spre[rt][nt][2], spre[rt][nt][3]};
+            for (int nt = 0; nt < 2; ++nt) X[rt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         // (past the last entry these re-read the last one: the same loads on
         // every path keep the compiler's wait counts exact)
         const int jn = j + 1 < m ? j + 1 : j;
-        if (seam_one_stage) seam_fetch<D, FAM, bf16>(seam_pf, a.x, chain, dk, sb_at(jn), a.w);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -553,10 +552,27 @@ k_compose_lean(ComposeArgs a) {
                     X[rt][nt] = mfma(al, xh[kb][nt], X[rt][nt]);
                 }
             }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) X[rt][nt][jj] += spre[rt][nt][jj];
+        // (every product is issued before the barrier, so that the B operands
+        // are dead in the staging phase)
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();  // every wave is past T_j and the seam staging
+        __builtin_amdgcn_sched_barrier(0);
+        // Staging.  The next window goes straight to LDS: its loads are in
+        // flight together with T's, and nothing holds them across a barrier.
+        // S_{j+1} is requested once T_{j+1} is in LDS, so the two never hold
+        // registers at once (scheduling barriers keep the compiler from
+        // hoisting the S loads), and S has the next seam phase to arrive.
         const int ln2 = lane_fresh();
+        if (seam_one_stage) seam_fetch<D, FAM, bf16>(seam_pf, a.x, chain, dk, sb_at(jn), a.w);
         t_load(jn, ln2);
-        s_load(jn, ln2);
+        if (seam_one_stage) seam_put_b<D, FAM>(sm, seam_pf, a.w);
+        __builtin_amdgcn_sched_barrier(0);
         t_put(ln2);
         __syncthreads();  // T_{j+1} in place
     }
