@@ -382,17 +382,18 @@ k_compose_dense(TreeArgs t) {
 // k_compose_dense, laid out so that two workgroups share a compute unit and
 // hide each other's waits.  One LDS copy of T (hi | lo bf16 rows) and bf16
 // seam staging keep a workgroup's LDS under half of the compute unit's; at most
-// 256 registers per lane.  Per entry j:
+// 256 registers per lane, no spills.  Per entry j:
 //   seam:    the state is advanced through entry j's window, staged in LDS
 //            during the previous staging phase (chunk form on the matrix
 //            cores);
-//   product: the state becomes the B operand, the accumulators take S_j
-//            (loaded during the previous staging phase), then S <- T_j S + S_j
-//            from the LDS copy;
+//   product: the state becomes the split B operand, S_j is requested, the
+//            accumulators run T_j S from the LDS copy and then take + S_j
+//            (the loads have the product's length to arrive);
 //   staging: once every wave is past the product, the next window and
 //            T_{j+1} are requested and written into LDS (the wait for them is
-//            the other workgroup's time on the compute unit), then S_{j+1}
-//            requested.
+//            the other workgroup's time on the compute unit).
+// Nothing prefetched is held in registers across a phase, which is what keeps
+// the register count at 256.
 template <int D, int FAM>
 __global__ void __launch_bounds__(D / 32 * 64, 2)
 k_compose_lean(ComposeArgs a) {
@@ -565,9 +566,6 @@ k_compose_lean(ComposeArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         // Staging.  The next window goes straight to LDS: its loads are in
         // flight together with T's, and nothing holds them across a barrier.
-        // S_{j+1} is requested once T_{j+1} is in LDS, so the two never hold
-        // registers at once (scheduling barriers keep the compiler from
-        // hoisting the S loads), and S has the next seam phase to arrive.
         const int ln2 = lane_fresh();
         if (seam_one_stage) seam_fetch<D, FAM, bf16>(seam_pf, a.x, chain, dk, sb_at(jn), a.w);
         t_load(jn, ln2);

@@ -374,9 +374,40 @@ __device__ void seam_chunk_bf16(f32x4 (&X)[D / 16][2], const SM &sm, int nt, flo
         }
     }
     const float lam = eg[SEAM_STAGE - 1];
-    // P = [K; Q] S0 (rows 0-7: K S0, rows 8-15: Q S0) and the Gram [K;Q][K;Q]^T
     using E = typename std::remove_cv<typename std::remove_reference<decltype(sm.k[0][0])>::type>::type;
     constexpr bool B16 = std::is_same<E, bf16>::value;
+    // The staged values the state update needs, read first (they do not
+    // depend on the state, so their LDS latency overlaps the products below):
+    // lane (r16, grp < 2) takes k rows 4 grp .. 4 grp + 3 of column 16 rt + r16
+    // (the A operand of K^T) and v rows 4 grp .. of its two columns.  The reads
+    // are unconditional (rows wrapped into the stage) and masked afterwards.
+    s4v ktv[RT];
+    float vv[2][4];
+    {
+        const int r0 = (4 * grp) & (SEAM_STAGE - 1);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            s4v k4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (B16)
+                    k4[e] = __builtin_bit_cast(short, sm.k[r0 + e][16 * rt + r16]);
+                else
+                    k4[e] = __builtin_bit_cast(short, (bf16)sm.k[r0 + e][16 * rt + r16]);
+            }
+            ktv[rt] = grp < 2 ? k4 : s4v{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int n2 = 0; n2 < 2; ++n2) {
+            const int col = c0 + 16 * n2 + r16;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const float v = (float)sm.v[r0 + jj][col < D ? col : D - 1];
+                vv[n2][jj] = (grp < 2 && !v_zero) ? v : 0.f;
+            }
+        }
+    }
+    // P = [K; Q] S0 (rows 0-7: K S0, rows 8-15: Q S0) and the Gram [K;Q][K;Q]^T
     const E *qk = r16 < 8 ? &sm.k[r16][0] : &sm.q[r16 - 8][0];
     f32x4 P[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     f32x4 G = {0.f, 0.f, 0.f, 0.f};
@@ -455,14 +486,9 @@ __device__ void seam_chunk_bf16(f32x4 (&X)[D / 16][2], const SM &sm, int nt, flo
     for (int n2 = 0; n2 < 2; ++n2) {
         const int col = c0 + 16 * n2 + r16;
         // Y rows 0-7 (lane groups 0, 1); zero in rows 8-15
-        f32x4 yv = {0.f, 0.f, 0.f, 0.f};
-        if (grp < 2) {
+        f32x4 yv;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int t = 4 * grp + jj;
-                yv[jj] = (v_zero ? 0.f : (float)sm.v[t][col < D ? col : D - 1]) - eg4[jj] * P[n2][jj];
-            }
-        }
+        for (int jj = 0; jj < 4; ++jj) yv[jj] = grp < 2 ? vv[n2][jj] - eg4[jj] * P[n2][jj] : 0.f;
         s4v yh, yl;
         split4v(yv, yh, yl);
         f32x4 R = {0.f, 0.f, 0.f, 0.f};
@@ -492,20 +518,9 @@ __device__ void seam_chunk_bf16(f32x4 (&X)[D / 16][2], const SM &sm, int nt, flo
         split4v(Rs, rh, rl);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            s4v kt = {0, 0, 0, 0};
-            if (grp < 2) {
-                if constexpr (B16)
-                    kt = s4v{__builtin_bit_cast(short, sm.k[4 * grp][16 * rt + r16]),
-                             __builtin_bit_cast(short, sm.k[4 * grp + 1][16 * rt + r16]),
-                             __builtin_bit_cast(short, sm.k[4 * grp + 2][16 * rt + r16]),
-                             __builtin_bit_cast(short, sm.k[4 * grp + 3][16 * rt + r16])};
-                else
-                    kt = bf4(sm.k[4 * grp][16 * rt + r16], sm.k[4 * grp + 1][16 * rt + r16],
-                             sm.k[4 * grp + 2][16 * rt + r16], sm.k[4 * grp + 3][16 * rt + r16]);
-            }
             f32x4 acc = X[rt][n2] * lam;
-            acc = mfma16(kt, rh, acc);
-            X[rt][n2] = mfma16(kt, rl, acc);
+            acc = mfma16(ktv[rt], rh, acc);
+            X[rt][n2] = mfma16(ktv[rt], rl, acc);
         }
     }
 }
