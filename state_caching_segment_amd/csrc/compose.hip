@@ -126,11 +126,13 @@ __device__ __forceinline__ float *seam_out(const TreeArgs &t, bool isS, int e, i
 }
 
 // One staged stage of nt seam tokens on the wave's columns.
-template <int D, int FAM, bool CHUNK>
-__device__ __forceinline__ void seam_stage_run(f32x4 (&X)[D / 16][2], const SeamSmem<D, FAM> &sm, int nt,
+template <int D, int FAM, bool CHUNK, typename SM>
+__device__ __forceinline__ void seam_stage_run(f32x4 (&X)[D / 16][2], const SM &sm, int nt,
                                                float *o_first, const ComposeArgs &a, int c0, int dk,
                                                float (*nm)[SEAM_STAGE][9], bool v_zero) {
-    if constexpr (CHUNK)
+    if constexpr (CHUNK && FAM == KDA)
+        seam_chunk_kda<D>(X, sm, nt, o_first, (int64_t)a.n_chains * dk, c0, dk, nm[0], nm[1], v_zero);
+    else if constexpr (CHUNK)
         seam_chunk_bf16<D, FAM>(X, sm, nt, o_first, (int64_t)a.n_chains * dk, c0, dk, nm[0], nm[1], v_zero);
     else
         seam_tokens<D, FAM>(X, sm, nt, o_first, (int64_t)a.n_chains * dk, c0, c0, v_zero, dk);
@@ -148,8 +150,9 @@ k_compose_dense(TreeArgs t) {
     constexpr int NV = D * D / 4 / 64 / NWT;  // 16-byte pieces of T per lane
     constexpr int RPW = D / NWT;              // T rows staged by one wave
     __shared__ __attribute__((aligned(16))) char tsm[2][TL::BYTES];
-    __shared__ SeamSmem<D, FAM> sm;
-    constexpr bool CHUNK_SEAM = !F32 && (FAM == DELTANET || FAM == GDN);
+    constexpr bool CHUNK_SEAM = !F32 && fam_dense(FAM);
+    // (KDA's chunk seam takes its window pre-decayed)
+    __shared__ typename std::conditional<CHUNK_SEAM && FAM == KDA, SeamSmemKda<D>, SeamSmem<D, FAM>>::type sm;
     __shared__ float seam_nm[CHUNK_SEAM ? NWT : 1][2][SEAM_STAGE][9];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
@@ -283,16 +286,21 @@ k_compose_dense(TreeArgs t) {
             if (sb >= 0 && seam_one_stage) {
                 // the whole window was fetched ahead: no loop around it, so the
                 // compiler's wait counts stay exact through this block
-                __syncthreads();
-                seam_put<D, FAM, TIN>(sm, seam_pf, dk, a.w);
-                __syncthreads();
-                seam_stage_run<D, FAM, CHUNK_SEAM>(X, sm, a.w, seam_out(t, isS, e, req, j0 + j, chain, 0, dk), a, c0,
-                                                   dk, seam_nm[wv], !isS);
+                if constexpr (!fam_vgate(FAM)) {
+                    __syncthreads();
+                    seam_put<D, FAM, TIN>(sm, seam_pf, dk, a.w);
+                    __syncthreads();
+                    seam_stage_run<D, FAM, CHUNK_SEAM>(X, sm, a.w, seam_out(t, isS, e, req, j0 + j, chain, 0, dk), a,
+                                                       c0, dk, seam_nm[wv], !isS);
+                }
             } else if (sb >= 0) {
                 for (int s0 = 0; s0 < a.w; s0 += SEAM_STAGE) {
                     const int nt = a.w - s0 < SEAM_STAGE ? a.w - s0 : SEAM_STAGE;
                     __syncthreads();
-                    stage_seam<D, FAM, TIN>(sm, a.x, chain, dk, sb + s0, nt);
+                    if constexpr (CHUNK_SEAM && FAM == KDA)
+                        stage_seam_kda<D, TIN>(sm, a.x, chain, dk, sb + s0, nt);
+                    else
+                        stage_seam<D, FAM, TIN>(sm, a.x, chain, dk, sb + s0, nt);
                     __syncthreads();
                     seam_stage_run<D, FAM, CHUNK_SEAM>(X, sm, nt, seam_out(t, isS, e, req, j0 + j, chain, s0, dk), a,
                                                        c0, dk, seam_nm[wv], !isS);

@@ -36,6 +36,67 @@ struct SeamSmemB {
     float beta[SEAM_STAGE];
 };
 
+// A stage of KDA seam tokens in the decayed forms the chunk seam uses: with
+// E_t the window's cumulative per-channel decay through token t and E_c that
+// of its last token, rows E_t o q_t, E_t o k_t, k_t / E_t, (E_c / E_t) o k_t,
+// v_t, and E_c itself.  (Tokens past nt are zero tokens with decay 1.)
+template <int D>
+struct SeamSmemKda {
+    float ql[SEAM_STAGE][D];
+    float kl[SEAM_STAGE][D];
+    float kb[SEAM_STAGE][D];
+    float kt[SEAM_STAGE][D];
+    float v[SEAM_STAGE][D];
+    float ecl[D];
+    float beta[SEAM_STAGE];
+};
+
+template <int D, typename TIN>
+__device__ void stage_seam_kda(SeamSmemKda<D> &sm, const Tok &x, int chain, int dk, int64_t tok0, int nt) {
+    const int tid = threadIdx.x;
+    const TIN *qp = reinterpret_cast<const TIN *>(x.q) + (int64_t)chain * x.cs;
+    const TIN *kp = reinterpret_cast<const TIN *>(x.k) + (int64_t)chain * x.cs;
+    const TIN *vp = reinterpret_cast<const TIN *>(x.v) + (int64_t)chain * x.cs;
+    const TIN *gp = reinterpret_cast<const TIN *>(x.g) + (int64_t)chain * x.gcs;
+    // one thread per channel (every launch has at least d threads): the
+    // window's 4 x SEAM_STAGE loads are all issued before any is used
+    if (tid < D) {
+        const int i = tid, ic = i < dk ? i : dk - 1;
+        float qv[SEAM_STAGE], kv[SEAM_STAGE], vv[SEAM_STAGE], gv[SEAM_STAGE];
+#pragma unroll
+        for (int t = 0; t < SEAM_STAGE; ++t) {
+            const int64_t tc = tok0 + (t < nt ? t : nt - 1);
+            qv[t] = ldf(qp + tc * x.ts + ic);
+            kv[t] = ldf(kp + tc * x.ts + ic);
+            vv[t] = ldf(vp + tc * x.ts + ic);
+            gv[t] = ldf(gp + tc * x.gts + ic);
+        }
+        float e[SEAM_STAGE], p = 1.f;
+#pragma unroll
+        for (int t = 0; t < SEAM_STAGE; ++t) {
+            const bool ok = t < nt && i < dk;
+            p *= ok ? expf(gv[t]) : 1.f;
+            e[t] = p;
+            if (!ok) qv[t] = kv[t] = vv[t] = 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < SEAM_STAGE; ++t) {
+            sm.ql[t][i] = e[t] * qv[t];
+            sm.kl[t][i] = e[t] * kv[t];
+            sm.kb[t][i] = kv[t] / e[t];
+            sm.kt[t][i] = kv[t] * (p / e[t]);
+            sm.v[t][i] = vv[t];
+        }
+        sm.ecl[i] = p;
+    }
+    if (tid < SEAM_STAGE) {
+        const int t = tid;
+        const int64_t tc = tok0 + (t < nt ? t : nt - 1);
+        const float bv = ldf(reinterpret_cast<const TIN *>(x.beta) + (int64_t)chain * x.bcs + tc * x.bts);
+        sm.beta[t] = t < nt ? bv : 1.f;
+    }
+}
+
 // Stage tokens tok0 .. tok0+nt-1 of `chain` into bf16 rows (scalar-gate
 // families; rows past nt are zero tokens with a = beta = 1).
 template <int D, int FAM>
@@ -521,6 +582,164 @@ __device__ void seam_chunk_bf16(f32x4 (&X)[D / 16][2], const SM &sm, int nt, flo
             f32x4 acc = X[rt][n2] * lam;
             acc = mfma16(ktv[rt], rh, acc);
             X[rt][n2] = mfma16(ktv[rt], rl, acc);
+        }
+    }
+}
+
+// Up to SEAM_STAGE seam tokens of KDA (per-channel decay before the delta
+// erase) with bf16-exact staged q, k, v, as one chunk on the matrix cores
+// (same article, section on seam windows).  With E_t the window's cumulative
+// per-channel decay through token t (staged by stage_seam<..., true>) and
+// S0 the state entering the window, the token recurrence
+//     S_t = (I - beta_t k_t k_t^T) diag(a_t) S_{t-1} + beta_t k_t v_t^T,
+//     o_t = S_t^T q_t
+// regroups into
+//     G_ti = sum_c k_tc k_ic E_tc / E_ic,   M_ti = sum_c q_tc k_ic E_tc / E_ic,
+//     R    = (I + diag(beta) tril(G, -1))^-1 diag(beta) (V - (E o K) S0),
+//     o_t  = ((E o Q) S0)_t + sum_{i<=t} M_ti R_i,
+//     S    = diag(E_c) S0 + (E_c / E o K)^T R,
+// where E o K scales row t of K by E_t channel-wise and E_c is the last
+// token's E.  The ratios E_t / E_i (t >= i) are decays and at most 1; the
+// factor 1 / E_i alone grows with the decay over at most SEAM_STAGE tokens,
+// the same bounded range as the build's Gram.  The decayed operands are not
+// bf16-exact: every product takes the three-pass split.  sNw, sMw: this
+// wave's 8 x 9 fp32 scratch; v_zero as in seam_chunk_bf16.
+template <int D>
+__device__ void seam_chunk_kda(f32x4 (&X)[D / 16][2], const SeamSmemKda<D> &sm, int nt, float *o_first,
+                               int64_t o_tok_stride, int c0, int dk, float (*sNw)[9], float (*sMw)[9],
+                               bool v_zero = false) {
+    constexpr int RT = D / 16, KB = D / 32;
+    const int lane = lane_fresh(), r16 = lane & 15, grp = lane >> 4;
+    const int tr = r16 & (SEAM_STAGE - 1);  // this lane's token row
+    // [E o K; E o Q] rows (A operand of P and of the Gram) and (K / E) rows
+    // (B operand of the Gram, zero in columns 8-15), split, per k block
+    bf16x8 lh[KB], ll[KB], bh[KB], bl[KB];
+    const float *lrow = r16 < 8 ? &sm.kl[tr][0] : &sm.ql[tr][0];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        float av[8], bv[8];
+        const f32x4 a0 = *reinterpret_cast<const f32x4 *>(lrow + 32 * kb + 4 * grp);
+        const f32x4 a1 = *reinterpret_cast<const f32x4 *>(lrow + 32 * kb + 16 + 4 * grp);
+        const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&sm.kb[tr][32 * kb + 4 * grp]);
+        const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&sm.kb[tr][32 * kb + 16 + 4 * grp]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            av[e] = a0[e];
+            av[4 + e] = a1[e];
+            bv[e] = r16 < 8 ? b0[e] : 0.f;
+            bv[4 + e] = r16 < 8 ? b1[e] : 0.f;
+        }
+        split8(av, lh[kb], ll[kb]);
+        split8(bv, bh[kb], bl[kb]);
+    }
+    // P = [E o K; E o Q] S0 and the Gram [E o K; E o Q] (K / E)^T
+    f32x4 P[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 G = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        G = mfma(lh[kb], bh[kb], G);
+        G = mfma(lh[kb], bl[kb], G);
+        G = mfma(ll[kb], bh[kb], G);
+#pragma unroll
+        for (int n2 = 0; n2 < 2; ++n2) {
+            float xv[8];
+            bf16x8 xh, xl;
+            acc_to_perm(X[2 * kb][n2], X[2 * kb + 1][n2], xv);
+            split8(xv, xh, xl);
+            P[n2] = mfma(lh[kb], xh, P[n2]);
+            P[n2] = mfma(lh[kb], xl, P[n2]);
+            P[n2] = mfma(ll[kb], xh, P[n2]);
+        }
+    }
+    // G in C layout: lane (r16 = i, grp) holds row 4 grp + jj.  Rows 0-7 give
+    // N (t > i), rows 8-15 give M (i <= t) for t = row - 8.
+    if (r16 < 8) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int row = 4 * grp + jj, t = row & 7, i = r16;
+            if (row < 8)
+                sNw[t][i] = t > i ? sm.beta[t] * G[jj] : 0.f;
+            else
+                sMw[t][i] = i <= t ? G[jj] : 0.f;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // row r16 of (I + N)^-1 diag(beta): y (I + N) = e_r, swept from the last row up
+    float y[SEAM_STAGE];
+#pragma unroll
+    for (int j = 0; j < SEAM_STAGE; ++j) y[j] = (j == r16) ? 1.f : 0.f;
+#pragma unroll
+    for (int i = SEAM_STAGE - 1; i > 0; --i)
+#pragma unroll
+        for (int j = 0; j < i; ++j) y[j] -= y[i] * sNw[i][j];
+    f32x4 arow = {0.f, 0.f, 0.f, 0.f}, mrow = {0.f, 0.f, 0.f, 0.f};
+    if (grp < 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = 4 * grp + e;
+            arow[e] = r16 < 8 ? (grp == 0 ? y[e] : y[4 + e]) * sm.beta[j] : 0.f;
+            mrow[e] = r16 >= 8 ? sMw[r16 - 8][j] : 0.f;
+        }
+    }
+    s4v ah, al, mh, ml;
+    split4v(arow, ah, al);
+    split4v(mrow, mh, ml);
+    // state update operands: (E_c / E o K)^T tiles (rows = channels 16 rt + r16,
+    // k = tokens 4 grp .. 4 grp + 3 for grp < 2) and E_c of this lane's rows
+    const int r0 = (4 * grp) & (SEAM_STAGE - 1);
+    s4v kth[RT], ktl[RT];
+    f32x4 ecr[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int ch = 16 * rt + r16;
+        f32x4 kt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float v = sm.kt[r0 + e][ch];
+            kt[e] = grp < 2 ? v : 0.f;
+        }
+        split4v(kt, kth[rt], ktl[rt]);
+        ecr[rt] = *reinterpret_cast<const f32x4 *>(&sm.ecl[16 * rt + 4 * grp]);
+    }
+#pragma unroll
+    for (int n2 = 0; n2 < 2; ++n2) {
+        const int col = c0 + 16 * n2 + r16;
+        // Y = V - (E o K) S0 in rows 0-7 (lane groups 0, 1); zero in rows 8-15
+        f32x4 yv;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const float v = v_zero ? 0.f : sm.v[r0 + jj][col < D ? col : D - 1];
+            yv[jj] = grp < 2 ? v - P[n2][jj] : 0.f;
+        }
+        s4v yh, yl;
+        split4v(yv, yh, yl);
+        f32x4 R = {0.f, 0.f, 0.f, 0.f};
+        R = mfma16(ah, yh, R);
+        R = mfma16(ah, yl, R);
+        R = mfma16(al, yh, R);
+        s4v rh, rl;
+        split4v(R, rh, rl);
+        // outputs, rows 8-15: o_t = ((E o Q) S0)_t + (M R)_t
+        f32x4 O = {0.f, 0.f, 0.f, 0.f};
+        O = mfma16(mh, rh, O);
+        O = mfma16(mh, rl, O);
+        O = mfma16(ml, rh, O);
+        if (grp >= 2 && col < dk) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int t = 4 * (grp - 2) + jj;
+                if (t < nt) o_first[t * o_tok_stride + col] = P[n2][jj] + O[jj];
+            }
+        }
+        // S = diag(E_c) S0 + (E_c / E o K)^T R  (R rows 8-15 are zero)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            f32x4 acc = X[rt][n2] * ecr[rt];
+            acc = mfma16(kth[rt], rh, acc);
+            acc = mfma16(kth[rt], rl, acc);
+            X[rt][n2] = mfma16(ktl[rt], rh, acc);
         }
     }
 }
