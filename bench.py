@@ -155,14 +155,14 @@ def cpu_baseline(wl, n_chains_sample, w):
                       f"(all pairs + compose + seams), {dt:.1f} s; scaled by chains"}
 
 
-def workload_text(name, wl, plan, C, d, w, req_tokens, n_build, hits):
+def workload_text(name, wl, plan, C, d, w, req_tokens, n_build, hits, mode_name):
     n_req = len(wl.requests)
     heads = "30 layers x 32 heads" if C == 960 else f"{C} heads"
     req = (f"one {req_tokens}-token request" if n_req == 1 else f"{n_req} requests, {req_tokens} tokens")
     if hits:
-        return (f"{wl.family} {wl.dtype}: build of {n_build} cold segment bodies + tree compose with w={w} seams "
-                f"over all {plan.n_slots} cached pairs: {C} chains ({heads}), d={d}, {req}")
-    return (f"{wl.family} pair build + seq compose with w={w} seams: {C} chains ({heads}), d={d}, {req}, "
+        return (f"{wl.family} {wl.dtype}: build of {n_build} cold segment bodies + {mode_name} compose with w={w} "
+                f"seams over all {plan.n_slots} cached pairs: {C} chains ({heads}), d={d}, {req}")
+    return (f"{wl.family} pair build + {mode_name} compose with w={w} seams: {C} chains ({heads}), d={d}, {req}, "
             f"{plan.n_slots} segments")
 
 
@@ -174,6 +174,9 @@ def main():
     ap.add_argument("--config", default="c4")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times), to scale HBM counters")
+    ap.add_argument("--compose", choices=("auto", "seq", "tree"), default="auto",
+                    help="compose mode; auto: the tree scan where the workload asks for it (cache hits) or where the "
+                         "request's chains are fewer than the compute units (latency-bound), else sequential")
     ap.add_argument("--cpu-chains", type=int, default=-1,
                     help="chains in the oracle's CPU-baseline sample (-1: two per host thread; 0: skip)")
     args = ap.parse_args()
@@ -221,7 +224,11 @@ def main():
     # the sequential compose.
     cold = np.concatenate([c for c in wl.cold]) if wl.cold else np.ones(plan.n_slots, bool)
     hits = not cold.all()
-    mode = hy.TREE if hits else hy.SEQ
+    if args.compose == "auto":
+        n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+        mode = hy.TREE if hits or plan.n_req * C < n_cu else hy.SEQ
+    else:
+        mode = hy.TREE if args.compose == "tree" else hy.SEQ
     if hits:
         hy.hypic_segment_build(L, x, plan.n_slots, sb, se, plan.max_seg_len, T, S, stream=stream)
         cb_idx = np.nonzero(cold)[0]
@@ -235,10 +242,8 @@ def main():
         bsb, bse, n_build, bT, bS = sb, se, plan.n_slots, T, S
         build_lens = plan.seg_end - plan.seg_begin
     max_build = int(build_lens.max())
-    ws, nws = None, 0
-    if mode == hy.TREE:
-        nws = hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, plan.n_req, plan.max_list_len, w)
-        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    nws = hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, plan.n_req, plan.max_list_len, w)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
 
     def step(ev=None, cmode=mode):
         if ev:
@@ -263,13 +268,13 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    seq_ms = None
-    if mode == hy.TREE:  # the sequential compose of the same lists, for comparison
-        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-        for i in range(args.steps):
-            step(sev[i], hy.SEQ)
-        torch.cuda.synchronize()
-        seq_ms = float(np.median([e[2].elapsed_time(e[3]) for e in sev]))
+    # the other compose mode on the same lists, for comparison
+    alt_mode = hy.SEQ if mode == hy.TREE else hy.TREE
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(sev[i], alt_mode)
+    torch.cuda.synchronize()
+    alt_ms = float(np.median([e[2].elapsed_time(e[3]) for e in sev]))
     b_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     c_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
     step_ms = wall * 1e3 / args.steps
@@ -313,9 +318,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": workload_text(args.config, wl, plan, C, d, w, req_tokens, n_build, hits),
+        "config": {"workload": workload_text(args.config, wl, plan, C, d, w, req_tokens, n_build, hits,
+                                               "tree" if mode == hy.TREE else "seq"),
                    "chains": C, "d": d, "request_tokens": req_tokens, "segments": plan.n_slots, "w": w,
-                   "built_segments": n_build, "built_tokens": build_tokens, "compose_mode": "tree" if hits else "seq",
+                   "built_segments": n_build, "built_tokens": build_tokens, "compose_mode": "tree" if mode == hy.TREE else "seq",
                    "state_dtype": "f32"},
         "build_ms": float(np.median(b_ms)),
         "build_ms_p10_p90": [float(np.percentile(b_ms, 10)), float(np.percentile(b_ms, 90))],
@@ -325,8 +331,7 @@ def main():
         "roofline": roof_build,
         "roofline_compose": roof_comp,
     }
-    if seq_ms is not None:
-        out["compose_seq_latency_ms"] = seq_ms
+    out["compose_alt"] = {"mode": "seq" if alt_mode == hy.SEQ else "tree", "ms": alt_ms}
     if args.cpu_chains != 0:
         import oracle
         n_cpu = 2 * oracle.max_threads() if args.cpu_chains < 0 else args.cpu_chains
