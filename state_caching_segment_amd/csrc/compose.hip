@@ -402,10 +402,16 @@ k_compose_dense(TreeArgs t) {
 //            the other workgroup's time on the compute unit).
 // Nothing prefetched is held in registers across a phase, which is what keeps
 // the register count at 256.
-template <int D, int FAM>
+//
+// SCAN: the tree compose's second phase on the same machinery.  The entries
+// are the request's block aggregates (slot req * NB + b of aggT / aggS, no
+// seams), and the state entering each block is stored to sin before its
+// product.
+template <int D, int FAM, bool SCAN = false>
 __global__ void __launch_bounds__(D / 32 * 64, 2)
-k_compose_lean(ComposeArgs a) {
+k_compose_lean(TreeArgs targ) {
     static_assert(D >= 64 && (FAM == DELTANET || FAM == GDN), "lean compose: d >= 64, scalar-gate erasing families");
+    const ComposeArgs a = targ.c;
     constexpr int NW = D / 32, RT = D / 16, KB = D / 32;
     using TL = DenseTLds<D, false>;
     constexpr int LDT = TL::LDT;
@@ -421,7 +427,8 @@ k_compose_lean(ComposeArgs a) {
     const int c0 = wv * 32;
     float *st = a.state + ((int64_t)req * a.n_chains + chain) * dk * dk;
     const int e0 = a.list_off[req];
-    const int m = a.list_off[req + 1] - e0;
+    const int len = a.list_off[req + 1] - e0;
+    const int m = SCAN ? (len + targ.B - 1) / targ.B : len;
 
     // pair ids and seam starts of 64 entries at a time, read back with readlane
     int win_base = 0, win_pid = 0;
@@ -429,8 +436,8 @@ k_compose_lean(ComposeArgs a) {
     auto win_load = [&](int b) {
         win_base = b;
         const int idx = b + lane < m ? b + lane : m - 1;
-        win_pid = a.pair_id[e0 + idx];
-        win_sb = a.has_seam ? a.seam_begin[e0 + idx] : -1;
+        win_pid = SCAN ? req * targ.NB + idx : a.pair_id[e0 + idx];
+        win_sb = (a.has_seam && !SCAN) ? a.seam_begin[e0 + idx] : -1;
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): settled here, not at every later use
     };
     auto pid_at = [&](int j) -> int64_t { return __builtin_amdgcn_readlane(win_pid, j - win_base); };
@@ -511,7 +518,23 @@ k_compose_lean(ComposeArgs a) {
         const int e = e0 + j;
         if (j + 2 >= win_base + 64) win_load(j);
         const int ln = lane_fresh(), lr16 = ln & 15, lgrp = ln >> 4;
-        if (a.has_seam) {
+        if constexpr (SCAN) {
+            // the state entering block j
+            const auto r = buffer_view(targ.sin + (((int64_t)req * targ.NB + j) * a.n_chains + chain) * dk * dk,
+                                       D * D * 4);
+            const int voff = ((int)((unsigned)ln >> 4) * 4 * D + c0 + (int)((unsigned)ln & 15)) * 4;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const float v = X[rt][nt][jj];
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff,
+                                                              ((16 * rt + jj) * D + 16 * nt) * 4, 0);
+                    }
+        }
+        if (a.has_seam && !SCAN) {
             const int64_t sb = sb_at(j);
             float *o_first = a.o + ((int64_t)e * a.w * a.n_chains + chain) * dk;
             if (sb >= 0 && seam_one_stage) {
@@ -751,7 +774,9 @@ template <int D, int FAM, typename TIN>
 static hipError_t launch_compose(const ComposeArgs &a, int n_req, hipStream_t st) {
     const dim3 grid((unsigned)(n_req * (int64_t)a.n_chains)), block(D / 32 * 64);
     if constexpr (std::is_same<TIN, bf16>::value && D >= 64 && (FAM == DELTANET || FAM == GDN)) {
-        hipLaunchKernelGGL((k_compose_lean<D, FAM>), grid, block, 0, st, a);
+        TreeArgs t{};
+        t.c = a;
+        hipLaunchKernelGGL((k_compose_lean<D, FAM, false>), grid, block, 0, st, t);
     } else if constexpr (fam_dense(FAM)) {
         TreeArgs t{};
         t.c = a;
@@ -777,8 +802,20 @@ static hipError_t launch_tree(const TreeArgs &t, int n_req, hipStream_t st) {
         hipLaunchKernelGGL((k_tree_block<D, FAM, TIN>), dim3(blocks), dim3(2 * D / 32 * 64), 0, st, t);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((k_tree_scan<D, TIN>), dim3((unsigned)(n_req * (int64_t)t.c.n_chains)), dim3(D / 32 * 64), 0, st,
-                       t);
+    if constexpr (std::is_same<TIN, bf16>::value && D >= 64 && fam_dense(FAM)) {
+        // the scan over dense block aggregates is a seam-free sequential
+        // compose of them (any dense family: no family-specific step remains)
+        TreeArgs ts = t;
+        ts.c.T = t.aggT;
+        ts.c.S = t.aggS;
+        ts.c.t_elems = (int64_t)t.c.dk * t.c.dk;
+        ts.c.has_seam = 0;
+        hipLaunchKernelGGL((k_compose_lean<D, GDN, true>), dim3((unsigned)(n_req * (int64_t)t.c.n_chains)),
+                           dim3(D / 32 * 64), 0, st, ts);
+    } else {
+        hipLaunchKernelGGL((k_tree_scan<D, TIN>), dim3((unsigned)(n_req * (int64_t)t.c.n_chains)),
+                           dim3(D / 32 * 64), 0, st, t);
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (t.c.has_seam) {
         hipLaunchKernelGGL((k_tree_fix<D>), dim3(blocks), dim3(D / 32 * 64), 0, st, t);
