@@ -756,6 +756,103 @@ k_tree_fix(TreeArgs t) {
     }
 }
 
+// phase 3 on the matrix cores (bf16 inputs, d >= 64): the block's seam
+// tokens, 64 at a time, as rows of P (their pulled-back queries), so that
+// O = P S_in is one product per wave on its 32 columns; o += O.  P is staged
+// once per workgroup through LDS as hi | lo bf16 rows (the layout the lean
+// compose uses for T); S_in is the split B operand.
+template <int D>
+__global__ void __launch_bounds__(D / 32 * 64)
+k_tree_fix_mma(TreeArgs t) {
+    constexpr int RT = D / 16, KB = D / 32, NW = D / 32;
+    constexpr int PR = 64;               // token rows per pass
+    constexpr int LDP = 2 * D + 8;       // bf16 per staged row: [hi | lo] + pad
+    constexpr int NV = PR * D / 4 / 64 / NW;  // 16-byte pieces of P per lane
+    __shared__ __attribute__((aligned(16))) bf16 psm[PR * LDP];
+    const ComposeArgs &a = t.c;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int r16 = lane & 15, grp = lane >> 4;
+    const int chain = blockIdx.x % a.n_chains;
+    const int rb = blockIdx.x / a.n_chains, req = rb / t.NB, blk = rb % t.NB;
+    constexpr int dk = D;
+    const int c0 = wv * 32;
+    const int e0 = a.list_off[req], len = a.list_off[req + 1] - e0;
+    const int j0 = blk * t.B;
+    if (j0 >= len) return;  // uniform over the workgroup
+    const int j1 = j0 + t.B < len ? j0 + t.B : len;
+    const int nrows = (j1 - j0) * a.w;
+    // S_in columns c0 .. c0+31 in the C layout, split as the B operand
+    bf16x8 xh[KB][2], xl[KB][2];
+    {
+        const auto r = buffer_view(t.sin + (((int64_t)req * t.NB + blk) * a.n_chains + chain) * dk * dk, D * D * 4);
+        const int voff = (grp * 4 * D + c0 + r16) * 4;
+        f32x4 X[RT][2];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    X[rt][nt][jj] = __builtin_bit_cast(
+                        float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, ((16 * rt + jj) * D + 16 * nt) * 4, 0));
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                float xv[8];
+                acc_to_perm(X[2 * kb][nt], X[2 * kb + 1][nt], xv);
+                split8(xv, xh[kb][nt], xl[kb][nt]);
+            }
+    }
+    for (int r0 = 0; r0 < nrows; r0 += PR) {
+        // stage P rows r0 .. r0 + 63 (token s of entry j0 + r / w); rows past
+        // the block or of entries without a seam are zero
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int item = (i * NW + wv) * 64 + lane, row = item / (D / 4), c4 = item % (D / 4);
+            const int r = r0 + row, j = j0 + r / a.w, sidx = r % a.w;
+            const bool ok = r < nrows && a.seam_begin[e0 + (j < j1 ? j : j1 - 1)] >= 0;
+            const int jc = ok ? j : j0, sc = ok ? sidx : 0;
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(
+                t.pvec + ((((int64_t)req * t.max_list + jc) * a.w + sc) * a.n_chains + chain) * dk + 4 * c4);
+            const int sub = c4 % 8, pos = 32 * (c4 / 8) + 8 * (sub % 4) + 4 * (sub / 4);
+            uint32_t h0, l0, h1, l1;
+            split2(ok ? v[0] : 0.f, ok ? v[1] : 0.f, h0, l0);
+            split2(ok ? v[2] : 0.f, ok ? v[3] : 0.f, h1, l1);
+            *reinterpret_cast<u32x2 *>(psm + row * LDP + pos) = u32x2{h0, h1};
+            *reinterpret_cast<u32x2 *>(psm + row * LDP + D + pos) = u32x2{l0, l1};
+        }
+        __syncthreads();
+        // O = P S_in for this wave's columns, then o += O
+#pragma unroll
+        for (int rt = 0; rt < PR / 16; ++rt) {
+            f32x4 O[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int off = (16 * rt + r16) * LDP + 32 * kb + 8 * grp;
+                const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(psm + off);
+                const bf16x8 al = *reinterpret_cast<const bf16x8 *>(psm + D + off);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    O[nt] = mfma(ah, xh[kb][nt], O[nt]);
+                    O[nt] = mfma(ah, xl[kb][nt], O[nt]);
+                    O[nt] = mfma(al, xh[kb][nt], O[nt]);
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int r = r0 + 16 * rt + 4 * grp + jj, j = j0 + r / a.w, sidx = r % a.w;
+                if (r < nrows && a.seam_begin[e0 + (j < j1 ? j : j1 - 1)] >= 0) {
+                    float *op = a.o + (((int64_t)(e0 + j) * a.w + sidx) * a.n_chains + chain) * dk + c0 + r16;
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) op[16 * nt] += O[nt][jj];
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
 // ---- launchers ----------------------------------------------------------------
 
 #define HY_DISPATCH_FAMILY(FN, ARGS, D, TIN)          \
@@ -818,7 +915,10 @@ static hipError_t launch_tree(const TreeArgs &t, int n_req, hipStream_t st) {
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (t.c.has_seam) {
-        hipLaunchKernelGGL((k_tree_fix<D>), dim3(blocks), dim3(D / 32 * 64), 0, st, t);
+        if constexpr (std::is_same<TIN, bf16>::value && D >= 64)
+            hipLaunchKernelGGL((k_tree_fix_mma<D>), dim3(blocks), dim3(D / 32 * 64), 0, st, t);
+        else
+            hipLaunchKernelGGL((k_tree_fix<D>), dim3(blocks), dim3(D / 32 * 64), 0, st, t);
         err = hipGetLastError();
     }
     return err;
