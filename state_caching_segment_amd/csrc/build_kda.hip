@@ -27,6 +27,7 @@
 namespace hy {
 
 constexpr int KC = 32;  // tokens per chunk
+constexpr float L2E = 1.4426950408889634f;  // log2(e): gates are kept in log2 units, exponentials are exp2
 
 template <int D, typename TIN>
 struct KdaCfg {
@@ -196,7 +197,7 @@ k_build_kda(BuildArgs a) {
         for (int e = 0; e < 8; ++e) {
             sK[it_t * LDK + it_i8 + e] = (OpT)kpre.get(e);
             sVT[(it_i8 + e) * LDT + it_t] = (OpT)vpre.get(e);
-            sG[it_t * LDG + it_i8 + e] = gpre.get(e);
+            sG[it_t * LDG + it_i8 + e] = gpre.get(e) * L2E;  // log2 units
         }
         if (wv == 0 && lane < KC) sBeta[lane] = (float)bpre;
         if (c0 + KC < n) prefetch(c0 + KC);
@@ -208,7 +209,7 @@ k_build_kda(BuildArgs a) {
                 s += sG[t * LDG + i];
                 sG[t * LDG + i] = s;
             }
-            sLam[i] = expf(s);
+            sLam[i] = __builtin_amdgcn_exp2f(s);
         }
         __syncthreads();
         // ---- K_L = exp(Gamma) * K (rows) and Kt^T = (exp(Gamma_c - Gamma) * K)^T
@@ -219,8 +220,8 @@ k_build_kda(BuildArgs a) {
                 const int i = i8 + e;
                 const float kv = (float)sK[t * LDK + i];
                 const float gm = sG[t * LDG + i];
-                put_split<F32>(sKL + t * LDK + i, LOK, kv * expf(gm));
-                put_split<F32>(sKtT + i * LDT + t, LOT, kv * expf(sG[(KC - 1) * LDG + i] - gm));
+                put_split<F32>(sKL + t * LDK + i, LOK, kv * __builtin_amdgcn_exp2f(gm));
+                put_split<F32>(sKtT + i * LDT + t, LOT, kv * __builtin_amdgcn_exp2f(sG[(KC - 1) * LDG + i] - gm));
             }
         }
         // ---- Gram with per-block reference tokens, scaled into the strictly lower L
@@ -235,8 +236,8 @@ k_build_kda(BuildArgs a) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float gr = sG[r * LDG + i0 + e];
-                    av[e] = (float)sK[ta * LDK + i0 + e] * expf(sG[ta * LDG + i0 + e] - gr);
-                    bv[e] = (float)sK[tb * LDK + i0 + e] * expf(gr - sG[tb * LDG + i0 + e]);
+                    av[e] = (float)sK[ta * LDK + i0 + e] * __builtin_amdgcn_exp2f(sG[ta * LDG + i0 + e] - gr);
+                    bv[e] = (float)sK[tb * LDK + i0 + e] * __builtin_amdgcn_exp2f(gr - sG[tb * LDG + i0 + e]);
                 }
                 acc = mma_split<F32>(av, bv, acc);
             }
