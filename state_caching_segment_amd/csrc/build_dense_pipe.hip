@@ -71,12 +71,16 @@ struct PipeCfg {
 typedef short s8v __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ void split4(const f32x4 &x, s4 &h, s4 &l) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const bf16 y = (bf16)x[e];
-        h[e] = __builtin_bit_cast(short, y);
-        l[e] = __builtin_bit_cast(short, (bf16)(x[e] - (float)y));
-    }
+    u32x2 hu, lu;
+    uint32_t a, b;
+    split2(x[0], x[1], a, b);
+    hu[0] = a;
+    lu[0] = b;
+    split2(x[2], x[3], a, b);
+    hu[1] = a;
+    lu[1] = b;
+    h = __builtin_bit_cast(s4, hu);
+    l = __builtin_bit_cast(s4, lu);
 }
 
 // C += A B on v_mfma_f32_16x16x16_bf16, operands split hi + lo (hi.hi + hi.lo +
