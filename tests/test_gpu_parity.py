@@ -72,6 +72,16 @@ def test_tree_compose(fam, dtype, d):
     check(wl, mode=hy.TREE, w=0, label=f"tree_{fam}_{dtype}_{d}_w0")
 
 
+@pytest.mark.parametrize("fam,d", [("gdn", 128), ("kda", 128), ("gla", 64)])
+@pytest.mark.parametrize("w", [5, 13])
+def test_seam_window_sizes(fam, d, w):
+    """Seam windows shorter than one staged stage (zero tokens pad the chunk)
+    and longer (two stages), sequential and tree compose."""
+    wl = small(fam, "bf16", d, lens=[70, 40, 33, 90, 61], w=w)
+    check(wl, label=f"{fam}_bf16_{d}_w{w}")
+    check(wl, mode=hy.TREE, label=f"{fam}_bf16_{d}_w{w}_tree")
+
+
 def test_slow_gate_gdn_d128():
     check(small("gdn", "bf16", 128, laws=workloads.SLOW_GDN_LAWS), label="slowgdn_bf16_128")
 
