@@ -61,11 +61,13 @@ def chain_inputs(wl, chains, t0, t1):
     return cm(wl.q), cm(wl.k), cm(wl.v), cm(wl.g), cm(wl.beta), gam
 
 
-def oracle_request(wl, chains, w=None, nthreads=0):
-    """The oracle's reuse path for every request, on the given chains."""
+def oracle_request(wl, chains, w=None, nthreads=0, reqs=None):
+    """The oracle's reuse path for every request (or the requests listed in
+    reqs), on the given chains."""
     w = wl.w if w is None else w
     out = []
-    for b in wl.requests:
+    for r in (range(len(wl.requests)) if reqs is None else reqs):
+        b = wl.requests[r]
         q, k, v, g, beta, gam = chain_inputs(wl, chains, int(b[0]), int(b[-1]))
         out.append(oracle.request_batch(wl.family, b - b[0], w, q, k, v, g, beta, gam, nthreads=nthreads))
     return out
@@ -86,8 +88,9 @@ def _rel(x, ref):
     return float(np.linalg.norm(x - ref) / nr) if nr > 0 else float(np.linalg.norm(x))
 
 
-def compare(wl, gpu, ref, chains, w=None):
-    """Max relative Frobenius errors per object kind; ref from oracle_request."""
+def compare(wl, gpu, ref, chains, w=None, reqs=None):
+    """Max relative Frobenius errors per object kind; ref from oracle_request
+    (with the same reqs)."""
     w = wl.w if w is None else w
     plan = gpu["plan"]
     T = gpu["T"].double().cpu().numpy()
@@ -95,7 +98,7 @@ def compare(wl, gpu, ref, chains, w=None):
     st = gpu["state"].double().cpu().numpy()
     O = gpu["O"].double().cpu().numpy()
     err = {"T": 0.0, "S": 0.0, "state": 0.0, "O": 0.0, "T_floor": 0}
-    for r, res in enumerate(ref):
+    for r, res in zip(range(len(ref)) if reqs is None else reqs, ref):
         e0 = int(plan.list_off[r])
         m = int(plan.list_off[r + 1]) - e0
         for j in range(m):

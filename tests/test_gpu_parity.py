@@ -4,8 +4,9 @@ oracle on the same seeded inputs.
 Tolerance: relative Frobenius error per object <= 1e-4 for fp32 inputs and
 <= 5e-3 for bf16 inputs with fp32 state.  Sizes span several 64-token chunks
 and ragged tails (lengths 9, 64+8, 65+8, 130, 513 ...), every family, d in
-{16, 32, 64, 128}; the full-size GDN request (960 chains, 32768 tokens) is
-checked on a seeded sample of chains.
+{16, 32, 64, 128}; the full-size GDN request (960 chains, 32768 tokens), the
+full C3 GLA request and a full KDA layer (16 requests of 100000 tokens, tree
+compose) are checked on samples of chains and requests.
 """
 import numpy as np
 import pytest
@@ -256,3 +257,20 @@ def test_gdn_full_request_sampled():
     err = compare(wl, gpu, ref, chains)
     print("c4 sampled", err, flush=True)
     assert_close(err, TOL["bf16"], "c4")
+
+
+def test_kda_c5_full_layer_sampled():
+    """KDA, one layer at full size: 32 heads, 16 requests of 100000 tokens in
+    128 lognormal segments each, w = 8; every segment built and every request
+    composed by the tree scan on the GPU (the kernels the KDA bench line
+    times); the oracle's full path for the first and last request on the
+    first and last head."""
+    wl = workloads.config("c5", device="cuda")
+    gpu = gpu_request(wl, mode=hy.TREE)
+    for key in ("T", "S", "state", "O"):
+        assert torch.isfinite(gpu[key]).all(), key
+    chains, reqs = [0, wl.n_chains - 1], [0, len(wl.requests) - 1]
+    ref = oracle_request(wl, chains, nthreads=len(chains), reqs=reqs)
+    err = compare(wl, gpu, ref, chains, reqs=reqs)
+    print("c5 sampled", err, flush=True)
+    assert_close(err, TOL["bf16"], "c5")
