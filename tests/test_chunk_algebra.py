@@ -60,3 +60,16 @@ def test_folded_decay_form_matches_oracle(fam, law):
         Tc, Sc = chunk_pair_folded(fam, k, v, g, beta)
         assert oracle.rel_fro(Tc, T) < 1e-11 or np.linalg.norm(T) < 1e-200, (n, law)
         assert oracle.rel_fro(Sc, S) < 1e-11, (n, law)
+
+
+def test_gdn_transition_is_decay_times_deltanet():
+    """With a scalar gate per token the decay commutes with every erasure, so
+    the oracle's GDN T of a segment is exp(sum of its log-gates) times its
+    DeltaNet T of the same keys and betas (a closed form tying the two
+    families' transition products together)."""
+    rng = np.random.default_rng(77)
+    for n in (1, 9, 64, 65, 300):
+        _, k, v, g, beta, _ = _inputs(rng, "gdn", n, 8, 6)
+        T, _ = oracle.pair("gdn", k, v, g, beta)
+        Tu, _ = oracle.pair("deltanet", k, v, None, beta)
+        assert oracle.rel_fro(np.exp(g.sum()) * Tu, T) < 1e-12, n
