@@ -201,7 +201,7 @@ def main():
 
     wl = workloads.config(args.config, device="cuda")
     w = wl.w
-    plan = request_plan(wl.requests, w)
+    plan = request_plan(wl.requests, w, slot_order="longest_first")
     d, C = wl.dk, wl.n_chains
     dev = "cuda"
     L = hy.layout(wl.family, wl.dtype, C, d)
@@ -222,7 +222,8 @@ def main():
     # associative tree scan over the full pair cache, which is built once
     # beforehand (untimed); the others time the build of every segment and
     # the sequential compose.
-    cold = np.concatenate([c for c in wl.cold]) if wl.cold else np.ones(plan.n_slots, bool)
+    cold = (np.concatenate([c for c in wl.cold])[plan.seg_index] if wl.cold
+            else np.ones(plan.n_slots, bool))  # per slot
     hits = not cold.all()
     if args.compose == "auto":
         n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
@@ -322,7 +323,7 @@ def main():
                                                "tree" if mode == hy.TREE else "seq"),
                    "chains": C, "d": d, "request_tokens": req_tokens, "segments": plan.n_slots, "w": w,
                    "built_segments": n_build, "built_tokens": build_tokens, "compose_mode": "tree" if mode == hy.TREE else "seq",
-                   "state_dtype": "f32"},
+                   "state_dtype": "f32", "slot_order": "longest_first"},
         "build_ms": float(np.median(b_ms)),
         "build_ms_p10_p90": [float(np.percentile(b_ms, 10)), float(np.percentile(b_ms, 90))],
         "compose_latency_ms": float(np.median(c_ms)),

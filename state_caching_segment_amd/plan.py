@@ -25,6 +25,7 @@ class Plan:
     pair_id: np.ndarray     # [n_entries] int32, pair slot of each entry
     seam_begin: np.ndarray  # [n_entries] int64, first seam token, -1 for a request's first entry
     w: int
+    seg_index: np.ndarray   # [n_slots] int64, the segment (numbered in request order) each slot holds
 
     @property
     def n_slots(self) -> int:
@@ -43,8 +44,18 @@ class Plan:
         return int(np.diff(self.list_off).max()) if self.n_req else 0
 
 
-def request_plan(requests: Sequence[np.ndarray], w: int) -> Plan:
-    """One pair slot per segment of every request, in request order."""
+def request_plan(requests: Sequence[np.ndarray], w: int, slot_order: str = "request") -> Plan:
+    """One pair slot per segment of every request.
+
+    slot_order "request": slots in request order.  "longest_first": slots
+    numbered by decreasing body length (ties in request order).  The build
+    launches one workgroup per (slot, chain) in slot order and the GPU hands
+    them out in that order, so longest-first is the longest-processing-time
+    rule: the long segments start first and the short ones fill in behind
+    them, which evens out the work per compute unit.  Entries reach their
+    slots through pair_id either way, so results do not depend on the order."""
+    if slot_order not in ("request", "longest_first"):
+        raise ValueError(f"unknown slot order {slot_order!r}")
     sb, se, po, pid, seam = [], [], [0], [], []
     for b in requests:
         b = np.asarray(b, dtype=np.int64)
@@ -59,5 +70,11 @@ def request_plan(requests: Sequence[np.ndarray], w: int) -> Plan:
             se.append(end)
             seam.append(start if (j > 0 and w > 0) else -1)
         po.append(len(pid))
-    return Plan(np.asarray(sb, np.int64), np.asarray(se, np.int64), np.asarray(po, np.int32),
-                np.asarray(pid, np.int32), np.asarray(seam, np.int64), w)
+    sb, se, pid = np.asarray(sb, np.int64), np.asarray(se, np.int64), np.asarray(pid, np.int32)
+    order = np.arange(len(sb), dtype=np.int64)
+    if slot_order == "longest_first" and len(sb):
+        order = np.argsort(-(se - sb), kind="stable")  # new slot i holds segment order[i]
+        rank = np.empty_like(order)
+        rank[order] = np.arange(len(order))
+        sb, se, pid = sb[order], se[order], rank[pid].astype(np.int32)
+    return Plan(sb, se, np.asarray(po, np.int32), pid, np.asarray(seam, np.int64), w, order)

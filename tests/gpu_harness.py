@@ -20,12 +20,12 @@ FLOOR = 2.0 ** -100
 TOL = {"f32": 1e-4, "bf16": 5e-3}
 
 
-def gpu_request(wl, w=None, stream=None, mode=None):
+def gpu_request(wl, w=None, stream=None, mode=None, slot_order="request"):
     """Build every segment body's pair, then compose each request with its seams
     (sequential compose, or the tree scan with mode=hy.TREE)."""
     mode = hy.SEQ if mode is None else mode
     w = wl.w if w is None else w
-    plan = request_plan(wl.requests, w)
+    plan = request_plan(wl.requests, w, slot_order=slot_order)
     dev = wl.k.device
     L = hy.layout(wl.family, wl.dtype, wl.n_chains, wl.dk)
     x = hy.tokens(wl.q, wl.k, wl.v, wl.g, wl.beta, wl.gamma)

@@ -132,3 +132,26 @@ def test_request_plan():
     assert p0.seg_begin.tolist() == [0, 100, 150, 300, 420] and (p0.seam_begin == -1).all()
     with pytest.raises(ValueError):
         request_plan([np.array([0, 100, 108])], 8)
+    assert p.seg_index.tolist() == [0, 1, 2, 3, 4]
+
+
+def test_request_plan_longest_first():
+    """Slots numbered by decreasing body length; every entry still reaches the
+    same token range through pair_id, and nothing else changes."""
+    rng = np.random.default_rng(5)
+    reqs, t = [], 0
+    for _ in range(4):
+        b = np.concatenate([[t], t + np.cumsum(rng.integers(20, 300, size=rng.integers(1, 7)))])
+        reqs.append(b)
+        t = int(b[-1])
+    p = request_plan(reqs, 8)
+    q = request_plan(reqs, 8, slot_order="longest_first")
+    lens = q.seg_end - q.seg_begin
+    assert (np.diff(lens) <= 0).all()
+    assert sorted(q.seg_index.tolist()) == list(range(p.n_slots))
+    assert (q.seg_begin == p.seg_begin[q.seg_index]).all() and (q.seg_end == p.seg_end[q.seg_index]).all()
+    assert (q.seg_begin[q.pair_id] == p.seg_begin[p.pair_id]).all()
+    assert (q.seg_end[q.pair_id] == p.seg_end[p.pair_id]).all()
+    assert (q.list_off == p.list_off).all() and (q.seam_begin == p.seam_begin).all()
+    with pytest.raises(ValueError):
+        request_plan(reqs, 8, slot_order="random")

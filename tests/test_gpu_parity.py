@@ -235,6 +235,24 @@ def test_resume_from_saved_prefix():
     assert torch.equal(o[1:], full["O"][1:])
 
 
+def test_longest_first_slots_give_identical_results():
+    """The pair slots numbered longest body first (the order bench.py builds
+    in) give bitwise the same pairs, states and seam outputs as request order."""
+    wl = workloads.make("gdn_slots", config_id=43, family="gdn", dtype="bf16", n_chains=4, d=128,
+                        lens=[130, 600, 9, 72, 300], w=8, laws=workloads.GDN_LAWS, device="cuda")
+    wl2 = workloads.make("gla_slots", config_id=44, family="gla", dtype="bf16", n_chains=4, d=64,
+                         lens=[130, 600, 9, 72, 300], w=8, laws=workloads.DIAG_LAWS, device="cuda")
+    for w_ in (wl, wl2):
+        a = gpu_request(w_)
+        b = gpu_request(w_, slot_order="longest_first")
+        pa, pb = a["plan"], b["plan"]
+        assert not (pa.seg_index == pb.seg_index).all()
+        for key in ("T", "S"):
+            assert torch.equal(a[key][torch.from_numpy(pa.pair_id).long()], b[key][torch.from_numpy(pb.pair_id).long()])
+        for key in ("state", "O"):
+            assert torch.equal(a[key], b[key]), key
+
+
 def test_bitwise_determinism():
     wl = small("gdn", "bf16", 128)
     a = gpu_request(wl)
