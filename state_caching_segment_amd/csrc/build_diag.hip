@@ -224,15 +224,17 @@ k_build_diag(BuildArgs a) {
     }
 }
 
-// ---- bf16 inputs: four token slices of a segment in parallel -----------------
+// ---- bf16 inputs: three token slices of a segment in parallel ----------------
 //
 // The state of a diagonal-decay segment is a sum over its tokens,
 //     S = sum_t diag(e^{Gamma_end - Gamma_t}) k_t v_t^T,
 // so a segment splits into slices whose partial states combine in order,
-//     S = L_3 (L_2 (L_1 S_0 + S_1) + S_2) + S_3,
+//     S = L_2 (L_1 S_0 + S_1) + S_2,
 // L_g the slice's decay product (one value per key channel).  One workgroup
-// per (segment, chain) holds four slice groups of d/32 waves each; group g
-// streams its quarter of the segment in 32-token chunks, last chunk first, so
+// per (segment, chain) holds three slice groups of d/32 waves each (three
+// rather than four: 12 waves leave each 168 registers, 16 would leave 128 and
+// spill); group g streams its third of the segment's 32-token chunks, a
+// contiguous run, last chunk first, so
 // the decay from a token to the slice's end is a product of per-token gates
 // that is known when the token is staged: within the chunk, a suffix product
 // over the lane's 8 tokens and across the 4 lanes holding the chunk's quarters;
@@ -245,7 +247,7 @@ k_build_diag(BuildArgs a) {
 template <int D>
 struct SliceCfg {
     static constexpr int NW = D / 32;  // waves per slice group (one per 32 columns / 32 channels)
-    static constexpr int NG = 4;       // slice groups
+    static constexpr int NG = 3;       // slice groups
     static constexpr int NT = NG * NW * 64;
     static constexpr int CS = 32;      // tokens per chunk
     static constexpr int LDK = D + 8;  // bf16 row stride of K~ and V rows
@@ -261,7 +263,7 @@ struct SliceCfg {
 };
 
 template <int D, int FAM>
-__global__ void __launch_bounds__(4 * (D / 32) * 64)
+__global__ void __launch_bounds__(SliceCfg<D>::NT)
 k_build_diag_slices(BuildArgs a) {
     using Cfg = SliceCfg<D>;
     constexpr int NW = Cfg::NW, NG = Cfg::NG, RT = D / 16, CS = Cfg::CS, LDK = Cfg::LDK;
