@@ -44,7 +44,10 @@ k_compose_seq(ComposeArgs a) {
     const int dk = a.dk, c0 = wv * 32;
     float *st = a.state + ((int64_t)req * a.n_chains + chain) * dk * dk;
     f32x4 X[D / 16][2];
-    load_tile<D>(X, st, dk, dk, c0, dk);
+    if constexpr (fam_dense(FAM))
+        load_tile<D>(X, st, dk, dk, c0, dk);
+    else
+        load_tile_buf<D>(X, st, dk, c0);
 
     const int e0 = a.list_off[req], e1 = a.list_off[req + 1];
     for (int e = e0; e < e1; ++e) {
@@ -64,12 +67,15 @@ k_compose_seq(ComposeArgs a) {
         const int64_t slot = a.pair_id[e];
         const float *Tp = a.T + (slot * a.n_chains + chain) * a.t_elems;
         const float *Sp = a.S + (slot * a.n_chains + chain) * dk * dk;
-        if (fam_dense(FAM))
+        if constexpr (fam_dense(FAM))
             apply_dense_T<D, F32>(X, Tp, dk, Sp, c0);
         else
-            apply_diag_T<D>(X, Tp, a.t_elems, dk, Sp, c0);
+            apply_diag_T_buf<D>(X, Tp, a.t_elems, dk, Sp, c0);
     }
-    store_tile<D>(X, st, dk, dk, c0, dk);
+    if constexpr (fam_dense(FAM))
+        store_tile<D>(X, st, dk, dk, c0, dk);
+    else
+        store_tile_buf<D>(X, st, dk, c0);
 }
 
 template <int D, int FAM, typename TIN>
@@ -672,17 +678,19 @@ k_tree_block(TreeArgs t) {
         const int64_t slot = a.pair_id[e];
         const float *Tp = a.T + (slot * a.n_chains + chain) * a.t_elems;
         const float *Sp = isS ? a.S + (slot * a.n_chains + chain) * dk * dk : nullptr;
-        if (fam_dense(FAM))
+        if constexpr (fam_dense(FAM))
             apply_dense_T<D, F32>(X, Tp, dk, Sp, c0);
         else
-            apply_diag_T<D>(X, Tp, a.t_elems, dk, Sp, c0);
+            apply_diag_T_buf<D>(X, Tp, a.t_elems, dk, Sp, c0);
     }
     const int64_t agg = (((int64_t)req * t.NB + blk) * a.n_chains + chain) * dk * dk;
-    store_tile<D>(X, (isS ? t.aggS : t.aggT) + agg, dk, dk, c0, dk);
+    store_tile_buf<D>(X, (isS ? t.aggS : t.aggT) + agg, dk, c0);
 }
 
-// phase 2: sequential scan over the block aggregates
-template <int D, typename TIN>
+// phase 2: sequential scan over the block aggregates.  DIAG: the family's T
+// is diagonal, so is every block aggregate's, and its diagonal (stride dk + 1
+// in the dense aggregate) scales the rows.
+template <int D, typename TIN, bool DIAG>
 __global__ void __launch_bounds__(D / 32 * 64)
 k_tree_scan(TreeArgs t) {
     constexpr bool F32 = std::is_same<TIN, float>::value;
@@ -692,15 +700,25 @@ k_tree_scan(TreeArgs t) {
     const int dk = a.dk, c0 = wv * 32;
     float *st = a.state + ((int64_t)req * a.n_chains + chain) * dk * dk;
     f32x4 X[D / 16][2];
-    load_tile<D>(X, st, dk, dk, c0, dk);
     const int len = a.list_off[req + 1] - a.list_off[req];
     const int nb = (len + t.B - 1) / t.B;
-    for (int b = 0; b < nb; ++b) {
-        const int64_t agg = (((int64_t)req * t.NB + b) * a.n_chains + chain) * dk * dk;
-        store_tile<D>(X, t.sin + agg, dk, dk, c0, dk);
-        apply_dense_T<D, F32>(X, t.aggT + agg, dk, t.aggS + agg, c0);
+    if constexpr (DIAG) {
+        load_tile_buf<D>(X, st, dk, c0);
+        for (int b = 0; b < nb; ++b) {
+            const int64_t agg = (((int64_t)req * t.NB + b) * a.n_chains + chain) * dk * dk;
+            store_tile_buf<D>(X, t.sin + agg, dk, c0);
+            apply_diag_agg<D>(X, t.aggT + agg, t.aggS + agg, dk, c0);
+        }
+        store_tile_buf<D>(X, st, dk, c0);
+    } else {
+        load_tile<D>(X, st, dk, dk, c0, dk);
+        for (int b = 0; b < nb; ++b) {
+            const int64_t agg = (((int64_t)req * t.NB + b) * a.n_chains + chain) * dk * dk;
+            store_tile<D>(X, t.sin + agg, dk, dk, c0, dk);
+            apply_dense_T<D, F32>(X, t.aggT + agg, dk, t.aggS + agg, c0);
+        }
+        store_tile<D>(X, st, dk, dk, c0, dk);
     }
-    store_tile<D>(X, st, dk, dk, c0, dk);
 }
 
 // phase 3: o_t += S_in^T p_t for the block's seam tokens
@@ -910,7 +928,7 @@ static hipError_t launch_tree(const TreeArgs &t, int n_req, hipStream_t st) {
         hipLaunchKernelGGL((k_compose_lean<D, GDN, true>), dim3((unsigned)(n_req * (int64_t)t.c.n_chains)),
                            dim3(D / 32 * 64), 0, st, ts);
     } else {
-        hipLaunchKernelGGL((k_tree_scan<D, TIN>), dim3((unsigned)(n_req * (int64_t)t.c.n_chains)),
+        hipLaunchKernelGGL((k_tree_scan<D, TIN, !fam_dense(FAM)>), dim3((unsigned)(n_req * (int64_t)t.c.n_chains)),
                            dim3(D / 32 * 64), 0, st, t);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;

@@ -849,4 +849,94 @@ __device__ __forceinline__ void apply_diag_T(f32x4 (&X)[D / 16][2], const float 
             }
 }
 
+// Tile I/O and the diagonal updates through buffer views of a dk x dk
+// row-major matrix: one per-lane offset, each row's offset a scalar (the
+// per-element 64-bit addresses of the plain helpers above would be held in
+// registers).  Reads of rows past dk return zero; loads zero the columns past
+// dk; the updates may leave values of no use there (every diagonal step keeps
+// columns apart), and stores skip them.
+template <int D>
+__device__ __forceinline__ void load_tile_buf(f32x4 (&X)[D / 16][2], const float *p, int dk, int c0) {
+    const int lane = lane_fresh(), r16 = lane & 15, grp = lane >> 4;
+    const auto r = buffer_view(p, dk * dk * 4);
+    const int v = (4 * grp * dk + c0 + r16) * 4;
+#pragma unroll
+    for (int rt = 0; rt < D / 16; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const float x = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(r, v, ((16 * rt + jj) * dk + 16 * nt) * 4, 0));
+                X[rt][nt][jj] = c0 + 16 * nt + r16 < dk ? x : 0.f;
+            }
+}
+
+template <int D>
+__device__ __forceinline__ void store_tile_buf(const f32x4 (&X)[D / 16][2], float *p, int dk, int c0) {
+    const int lane = lane_fresh(), r16 = lane & 15, grp = lane >> 4;
+    const auto r = buffer_view(p, dk * dk * 4);
+    const int v = (4 * grp * dk + c0 + r16) * 4;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        if (c0 + 16 * nt + r16 >= dk) continue;
+#pragma unroll
+        for (int rt = 0; rt < D / 16; ++rt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const float x = X[rt][nt][jj];  // (copied out: bit_cast of a vector element reads element 0)
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, v,
+                                                      ((16 * rt + jj) * dk + 16 * nt) * 4, 0);
+            }
+    }
+}
+
+// X <- diag(T) X + A, T and A dense dk x dk, the diagonal of T at stride dk + 1
+template <int D>
+__device__ __forceinline__ void apply_diag_agg(f32x4 (&X)[D / 16][2], const float *T, const float *A, int dk, int c0) {
+    const int lane = lane_fresh(), r16 = lane & 15, grp = lane >> 4;
+    const auto rT = buffer_view(T, dk * dk * 4);
+    const auto rA = buffer_view(A, dk * dk * 4);
+    const int vT = 4 * grp * (dk + 1) * 4, vA = (4 * grp * dk + c0 + r16) * 4;
+#pragma unroll
+    for (int rt = 0; rt < D / 16; ++rt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int r0 = 16 * rt + jj;
+            const float tv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rT, vT, r0 * (dk + 1) * 4, 0));
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const float av = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(rA, vA, (r0 * dk + 16 * nt) * 4, 0));
+                X[rt][nt][jj] = tv * X[rt][nt][jj] + av;
+            }
+        }
+}
+
+// X <- diag(T) X + add for a cached diagonal T (t_elems 1: a scalar; dk: a
+// vector) and add dense dk x dk or null (zero)
+template <int D>
+__device__ __forceinline__ void apply_diag_T_buf(f32x4 (&X)[D / 16][2], const float *T, int64_t t_elems, int dk,
+                                                 const float *add, int c0) {
+    const int lane = lane_fresh(), r16 = lane & 15, grp = lane >> 4;
+    const bool vec = t_elems != 1;
+    const auto rT = buffer_view(T, (int)t_elems * 4);
+    const auto rA = buffer_view(add, add ? dk * dk * 4 : 0);
+    const int vT = vec ? 4 * grp * 4 : 0, vA = (4 * grp * dk + c0 + r16) * 4;
+#pragma unroll
+    for (int rt = 0; rt < D / 16; ++rt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int r0 = 16 * rt + jj;
+            const float tv =
+                __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rT, vT, vec ? r0 * 4 : 0, 0));
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const float av = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(rA, vA, (r0 * dk + 16 * nt) * 4, 0));
+                X[rt][nt][jj] = tv * X[rt][nt][jj] + av;
+            }
+        }
+}
+
 }  // namespace hy
