@@ -273,7 +273,7 @@ k_compose_dense(TreeArgs t) {
             identity_tile<D>(X, c0);
         }
     } else {
-        load_tile<D>(X, st, dk, dk, c0, dk);
+        load_tile_buf<D>(X, st, dk, c0);
     }
     if (m > 0) {
         win_load(0);
@@ -385,9 +385,14 @@ k_compose_dense(TreeArgs t) {
     }
     if (TREE) {
         const int64_t agg = (((int64_t)req * t.NB + blk) * a.n_chains + chain) * dk * dk;
-        store_tile<D>(X, (isS ? t.aggS : t.aggT) + agg, dk, dk, c0, dk);
+        // (fp32 inputs keep the plain stores here: in that instantiation the
+        // buffer form spills more, not less)
+        if constexpr (F32)
+            store_tile<D>(X, (isS ? t.aggS : t.aggT) + agg, dk, dk, c0, dk);
+        else
+            store_tile_buf<D>(X, (isS ? t.aggS : t.aggT) + agg, dk, c0);
     } else {
-        store_tile<D>(X, st, dk, dk, c0, dk);
+        store_tile_buf<D>(X, st, dk, c0);
     }
 }
 
