@@ -830,25 +830,6 @@ __device__ __forceinline__ void apply_dense_T(f32x4 (&X)[D / 16][2], const float
         }
 }
 
-// Tile <- diag(T) Tile (+ add), T a scalar (t_elems == 1) or a dk-vector.
-template <int D>
-__device__ __forceinline__ void apply_diag_T(f32x4 (&X)[D / 16][2], const float *T, int64_t t_elems, int dk,
-                                             const float *add, int c0) {
-    const int lane = lane_id(), r16 = lane & 15, grp = lane >> 4;
-#pragma unroll
-    for (int rt = 0; rt < D / 16; ++rt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int row = 16 * rt + 4 * grp + jj, col = c0 + 16 * nt + r16;
-                const int rc = row < dk ? row : dk - 1, cc = col < dk ? col : dk - 1;
-                const float tv = t_elems == 1 ? T[0] : T[rc];
-                const float av = add ? add[rc * dk + cc] : 0.f;
-                if (row < dk && col < dk) X[rt][nt][jj] = tv * X[rt][nt][jj] + av;
-            }
-}
-
 // Tile I/O and the diagonal updates through buffer views of a dk x dk
 // row-major matrix: one per-lane offset, each row's offset a scalar (the
 // per-element 64-bit addresses of the plain helpers above would be held in
