@@ -59,8 +59,8 @@ def test_kda(dtype, d):
 
 
 @pytest.mark.parametrize("fam,dtype,d", [("gdn", "bf16", 128), ("kda", "bf16", 128), ("gla", "bf16", 64),
-                                         ("retnet", "f32", 32), ("deltanet", "f32", 16), ("mamba2", "bf16", 64),
-                                         ("linear", "f32", 64)])
+                                         ("gla", "bf16", 128), ("retnet", "f32", 32), ("retnet", "bf16", 16),
+                                         ("deltanet", "f32", 16), ("mamba2", "bf16", 64), ("linear", "f32", 64)])
 def test_tree_compose(fam, dtype, d):
     """Tree-scan compose (several requests of unequal length, lists not a
     multiple of the block size) against the oracle's left-to-right path."""
@@ -127,8 +127,10 @@ def test_retnet_c2_closed_form_and_naive_addition():
 
 
 def test_gla_c3_sampled():
+    """The full C3 request, sequential compose and the tree scan bench.py times."""
     wl = workloads.config("c3", device="cuda")
     check(wl, chains=[0, 5, 10, 15])
+    check(wl, chains=[0, 15], mode=hy.TREE, label="c3_tree")
 
 
 def test_compose_and_seam_from_oracle_pairs_all_families():
