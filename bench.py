@@ -176,7 +176,8 @@ def main():
                     help="only run a plain device-to-device copy of MIB MiB (5 times), to scale HBM counters")
     ap.add_argument("--compose", choices=("auto", "seq", "tree"), default="auto",
                     help="compose mode; auto: the tree scan where the workload asks for it (cache hits) or where the "
-                         "request's chains are fewer than the compute units (latency-bound), else sequential")
+                         "request's chains are fewer than the compute units and its list has at least 16 entries "
+                         "(latency-bound), else sequential")
     ap.add_argument("--cpu-chains", type=int, default=-1,
                     help="chains in the oracle's CPU-baseline sample (-1: two per host thread; 0: skip)")
     args = ap.parse_args()
@@ -227,7 +228,9 @@ def main():
     hits = not cold.all()
     if args.compose == "auto":
         n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
-        mode = hy.TREE if hits or plan.n_req * C < n_cu else hy.SEQ
+        # the tree's parallel blocks pay only on long lists: C3's 32 entries on 16
+        # chains (0.24 ms against 0.44), not C2's 8 entries on 8 chains
+        mode = hy.TREE if hits or (plan.n_req * C < n_cu and plan.max_list_len >= 16) else hy.SEQ
     else:
         mode = hy.TREE if args.compose == "tree" else hy.SEQ
     if hits:
