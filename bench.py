@@ -179,7 +179,8 @@ def main():
                          "request's chains are fewer than the compute units and its list has at least 16 entries "
                          "(latency-bound), else sequential")
     ap.add_argument("--cpu-chains", type=int, default=-1,
-                    help="chains in the oracle's CPU-baseline sample (-1: two per host thread; 0: skip)")
+                    help="chains in the oracle's CPU-baseline sample (-1: four per host thread, about 13 s of "
+                         "host work at the default workload; 0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path shards by chain with no "
@@ -338,7 +339,7 @@ def main():
     out["compose_alt"] = {"mode": "seq" if alt_mode == hy.SEQ else "tree", "ms": alt_ms}
     if args.cpu_chains != 0:
         import oracle
-        n_cpu = 2 * oracle.max_threads() if args.cpu_chains < 0 else args.cpu_chains
+        n_cpu = 4 * oracle.max_threads() if args.cpu_chains < 0 else args.cpu_chains
         out["cpu_baseline"] = cpu_baseline(wl, min(n_cpu, C), w)
     print(json.dumps(out), flush=True)
 
