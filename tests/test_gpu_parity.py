@@ -255,10 +255,15 @@ def test_longest_first_slots_give_identical_results():
             assert torch.equal(a[key], b[key]), key
 
 
-def test_bitwise_determinism():
-    wl = small("gdn", "bf16", 128)
-    a = gpu_request(wl)
-    b = gpu_request(wl)
+@pytest.mark.parametrize("fam,d,mode", [("gdn", 128, "seq"), ("gla", 128, "tree"), ("kda", 128, "tree"),
+                                        ("retnet", 64, "seq")])
+def test_bitwise_determinism(fam, d, mode):
+    """Two runs of the same request give bitwise equal pairs, states and seam
+    outputs (no atomics or order-dependent sums anywhere on the path)."""
+    wl = small(fam, "bf16", d)
+    m = hy.TREE if mode == "tree" else hy.SEQ
+    a = gpu_request(wl, mode=m)
+    b = gpu_request(wl, mode=m)
     for key in ("T", "S", "state", "O"):
         assert torch.equal(a[key], b[key]), key
 
