@@ -261,6 +261,12 @@ k_compose_dense(TreeArgs t) {
     // one staging stage and the gate is a scalar per token
     SeamPrefetch<D, TIN> seam_pf;
     const bool seam_one_stage = !fam_vgate(FAM) && a.has_seam && a.w <= SEAM_STAGE;
+    // KDA (bf16 inputs), sequential mode: the next window is fetched ahead
+    // too, one channel per thread, and staged in its decayed forms at the
+    // seam (in tree mode, eight waves at 256 registers, it would spill)
+    constexpr bool KDA_PF = CHUNK_SEAM && FAM == KDA && !TREE;
+    KdaSeamPrefetch<D, TIN> kda_pf;
+    const bool kda_one_stage = KDA_PF && a.has_seam && a.w <= SEAM_STAGE;
 
     f32x4 X[RT][2];
     if (TREE) {
@@ -282,6 +288,8 @@ k_compose_dense(TreeArgs t) {
         t_put(0);
         t_load(m > 1 ? 1 : 0);
         if (seam_one_stage) seam_fetch<D, FAM, TIN>(seam_pf, a.x, chain, dk, sb_at(0), a.w);
+        if constexpr (KDA_PF)
+            if (kda_one_stage) seam_fetch_kda<D, TIN>(kda_pf, a.x, chain, dk, sb_at(0), a.w);
         __syncthreads();
     }
     for (int j = 0; j < m; ++j) {
@@ -295,6 +303,14 @@ k_compose_dense(TreeArgs t) {
                 if constexpr (!fam_vgate(FAM)) {
                     __syncthreads();
                     seam_put<D, FAM, TIN>(sm, seam_pf, dk, a.w);
+                    __syncthreads();
+                    seam_stage_run<D, FAM, CHUNK_SEAM>(X, sm, a.w, seam_out(t, isS, e, req, j0 + j, chain, 0, dk), a,
+                                                       c0, dk, seam_nm[wv], !isS);
+                }
+            } else if (sb >= 0 && kda_one_stage) {
+                if constexpr (KDA_PF) {
+                    __syncthreads();
+                    seam_put_kda<D, TIN>(sm, kda_pf, dk, a.w);
                     __syncthreads();
                     seam_stage_run<D, FAM, CHUNK_SEAM>(X, sm, a.w, seam_out(t, isS, e, req, j0 + j, chain, 0, dk), a,
                                                        c0, dk, seam_nm[wv], !isS);
@@ -333,6 +349,8 @@ k_compose_dense(TreeArgs t) {
             const int jn = j + 1 < m ? j + 1 : j;
             s_load(jn);
             if (seam_one_stage) seam_fetch<D, FAM, TIN>(seam_pf, a.x, chain, dk, sb_at(jn), a.w);
+            if constexpr (KDA_PF)
+                if (kda_one_stage) seam_fetch_kda<D, TIN>(kda_pf, a.x, chain, dk, sb_at(jn), a.w);
             const float *tf = reinterpret_cast<const float *>(tsm[j & 1]);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
@@ -363,6 +381,8 @@ k_compose_dense(TreeArgs t) {
             const int jn = j + 1 < m ? j + 1 : j;
             s_load(jn);
             if (seam_one_stage) seam_fetch<D, FAM, TIN>(seam_pf, a.x, chain, dk, sb_at(jn), a.w);
+            if constexpr (KDA_PF)
+                if (kda_one_stage) seam_fetch_kda<D, TIN>(kda_pf, a.x, chain, dk, sb_at(jn), a.w);
             const bf16 *th = reinterpret_cast<const bf16 *>(tsm[j & 1]);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)

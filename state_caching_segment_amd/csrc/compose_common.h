@@ -336,6 +336,74 @@ __device__ __forceinline__ void seam_fetch(SeamPrefetch<D, TIN> &p, const Tok &x
     }
 }
 
+// KDA seam stage fetched ahead into registers: thread i holds channel i % D of
+// every token of the stage (the layout the staging's per-channel decay
+// product needs), as raw bits; threads past d repeat loads and write nothing.
+// When the entry has no seam (tok0 < 0) every view is empty and the values
+// read as zero; so do tokens past nt.
+template <int D, typename TIN>
+struct KdaSeamPrefetch {
+    uint32_t q[SEAM_STAGE], k[SEAM_STAGE], v[SEAM_STAGE], g[SEAM_STAGE];
+    uint32_t b;  // beta of token tid (threads tid < SEAM_STAGE)
+};
+
+template <int D, typename TIN>
+__device__ __forceinline__ void seam_fetch_kda(KdaSeamPrefetch<D, TIN> &p, const Tok &x, int chain, int dk,
+                                               int64_t tok0, int nt) {
+    const int tid = threadIdx.x, i = tid % D, ic = i < dk ? i : dk - 1;
+    const bool on = tok0 >= 0;
+    const int64_t tb = on ? tok0 : 0;
+    const int rb = on ? (int)(((int64_t)(nt - 1) * x.ts + dk) * sizeof(TIN)) : 0;
+    const int gb = on ? (int)(((int64_t)(nt - 1) * x.gts + dk) * sizeof(TIN)) : 0;
+    const int64_t base = (int64_t)chain * x.cs + tb * x.ts;
+    const auto rq = buffer_view(reinterpret_cast<const TIN *>(x.q) + base, rb);
+    const auto rk = buffer_view(reinterpret_cast<const TIN *>(x.k) + base, rb);
+    const auto rv = buffer_view(reinterpret_cast<const TIN *>(x.v) + base, rb);
+    const auto rg = buffer_view(reinterpret_cast<const TIN *>(x.g) + (int64_t)chain * x.gcs + tb * x.gts, gb);
+#pragma unroll
+    for (int t = 0; t < SEAM_STAGE; ++t) {
+        const int off = (int)(((int64_t)t * x.ts + ic) * sizeof(TIN));
+        p.q[t] = buffer_scalar_bits<TIN>(rq, off);
+        p.k[t] = buffer_scalar_bits<TIN>(rk, off);
+        p.v[t] = buffer_scalar_bits<TIN>(rv, off);
+        p.g[t] = buffer_scalar_bits<TIN>(rg, (int)(((int64_t)t * x.gts + ic) * sizeof(TIN)));
+    }
+    const int tt = tid % SEAM_STAGE;
+    const auto rbeta = buffer_view(reinterpret_cast<const TIN *>(x.beta) + (int64_t)chain * x.bcs + tb * x.bts,
+                                   on ? (int)(((int64_t)(nt - 1) * x.bts + 1) * sizeof(TIN)) : 0);
+    p.b = buffer_scalar_bits<TIN>(rbeta, (int)((int64_t)tt * x.bts * sizeof(TIN)));
+}
+
+// Stage a fetched KDA seam window in the decayed forms (the arithmetic of
+// stage_seam_kda, from registers).
+template <int D, typename TIN>
+__device__ __forceinline__ void seam_put_kda(SeamSmemKda<D> &sm, const KdaSeamPrefetch<D, TIN> &p, int dk, int nt) {
+    const int tid = threadIdx.x;
+    if (tid < D) {
+        const int i = tid;
+        float qv[SEAM_STAGE], kv[SEAM_STAGE], vv[SEAM_STAGE], e[SEAM_STAGE], pr = 1.f;
+#pragma unroll
+        for (int t = 0; t < SEAM_STAGE; ++t) {
+            const bool ok = t < nt && i < dk;
+            pr *= ok ? expf(scalar_from_bits<TIN>(p.g[t])) : 1.f;
+            e[t] = pr;
+            qv[t] = ok ? scalar_from_bits<TIN>(p.q[t]) : 0.f;
+            kv[t] = ok ? scalar_from_bits<TIN>(p.k[t]) : 0.f;
+            vv[t] = ok ? scalar_from_bits<TIN>(p.v[t]) : 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < SEAM_STAGE; ++t) {
+            sm.ql[t][i] = e[t] * qv[t];
+            sm.kl[t][i] = e[t] * kv[t];
+            sm.kb[t][i] = kv[t] / e[t];
+            sm.kt[t][i] = kv[t] * (pr / e[t]);
+            sm.v[t][i] = vv[t];
+        }
+        sm.ecl[i] = pr;
+    }
+    if (tid < SEAM_STAGE) sm.beta[tid] = tid < nt ? scalar_from_bits<TIN>(p.b) : 1.f;
+}
+
 // Write a fetched stage into the LDS staging area (zero tokens past nt).
 template <int D, int FAM, typename TIN>
 __device__ __forceinline__ void seam_put(SeamSmem<D, FAM> &sm, const SeamPrefetch<D, TIN> &p, int dk, int nt) {
