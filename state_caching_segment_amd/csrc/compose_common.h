@@ -75,7 +75,7 @@ __device__ void stage_seam_kda(SeamSmemKda<D> &sm, const Tok &x, int chain, int 
 #pragma unroll
         for (int t = 0; t < SEAM_STAGE; ++t) {
             const bool ok = t < nt && i < dk;
-            p *= ok ? expf(gv[t]) : 1.f;
+            p *= ok ? __builtin_amdgcn_exp2f(gv[t] * 1.4426950408889634f) : 1.f;  // e^g as 2^(g log2 e)
             e[t] = p;
             if (!ok) qv[t] = kv[t] = vv[t] = 0.f;
         }
@@ -385,7 +385,7 @@ __device__ __forceinline__ void seam_put_kda(SeamSmemKda<D> &sm, const KdaSeamPr
 #pragma unroll
         for (int t = 0; t < SEAM_STAGE; ++t) {
             const bool ok = t < nt && i < dk;
-            pr *= ok ? expf(scalar_from_bits<TIN>(p.g[t])) : 1.f;
+            pr *= ok ? __builtin_amdgcn_exp2f(scalar_from_bits<TIN>(p.g[t]) * 1.4426950408889634f) : 1.f;
             e[t] = pr;
             qv[t] = ok ? scalar_from_bits<TIN>(p.q[t]) : 0.f;
             kv[t] = ok ? scalar_from_bits<TIN>(p.k[t]) : 0.f;
