@@ -50,10 +50,28 @@ k_compose_seq(ComposeArgs a) {
         load_tile_buf<D>(X, st, dk, c0);
 
     const int e0 = a.list_off[req], e1 = a.list_off[req + 1];
+    // a window that fits one stage is fetched one entry ahead into registers
+    // (not for a per-channel gate: measured slower here, 0.49 ms against 0.44
+    // on a 16-chain GLA request, while the tree's block phase gains)
+    SeamPrefetch<D, TIN> pf;
+    const bool one = !fam_vgate(FAM) && a.has_seam && a.w <= SEAM_STAGE;
+    // (the seam tokens, gamma included, exist only when the call has seams)
+    const float rg = (FAM == RETNET && one) ? a.x.gamma[chain] : 1.f;
+    if (one && e0 < e1) seam_fetch<D, FAM, TIN>(pf, a.x, chain, dk, a.seam_begin[e0], a.w);
     for (int e = e0; e < e1; ++e) {
         if (a.has_seam) {
             const int64_t sb = a.seam_begin[e];
-            if (sb >= 0) {
+            if (one) {
+                if (sb >= 0) {
+                    __syncthreads();
+                    seam_put<D, FAM, TIN>(sm, pf, dk, a.w, rg);
+                    __syncthreads();
+                }
+                seam_fetch<D, FAM, TIN>(pf, a.x, chain, dk, e + 1 < e1 ? a.seam_begin[e + 1] : -1, a.w);
+                if (sb >= 0)
+                    seam_tokens<D, FAM>(X, sm, a.w, a.o + ((int64_t)e * a.w * a.n_chains + chain) * dk,
+                                        (int64_t)a.n_chains * dk, c0, c0, false, dk);
+            } else if (sb >= 0) {
                 for (int s0 = 0; s0 < a.w; s0 += SEAM_STAGE) {
                     const int nt = a.w - s0 < SEAM_STAGE ? a.w - s0 : SEAM_STAGE;
                     __syncthreads();
@@ -683,9 +701,28 @@ k_tree_block(TreeArgs t) {
     } else {
         identity_tile<D>(X, c0);
     }
+    // a window that fits one stage is fetched one entry ahead into registers
+    SeamPrefetch<D, TIN> pf;
+    const bool one = a.has_seam && a.w <= SEAM_STAGE;
+    // (the seam tokens, gamma included, exist only when the call has seams)
+    const float rg = (FAM == RETNET && one) ? a.x.gamma[chain] : 1.f;
+    if (one) seam_fetch<D, FAM, TIN>(pf, a.x, chain, dk, a.seam_begin[e0 + j0], a.w);
     for (int j = j0; j < j1; ++j) {
         const int e = e0 + j;
-        if (a.has_seam) {
+        if (a.has_seam && one) {
+            const int64_t sb = a.seam_begin[e];
+            if (sb >= 0) {
+                __syncthreads();
+                seam_put<D, FAM, TIN>(sm, pf, dk, a.w, rg);
+                __syncthreads();
+            }
+            seam_fetch<D, FAM, TIN>(pf, a.x, chain, dk, j + 1 < j1 ? a.seam_begin[e + 1] : -1, a.w);
+            if (sb >= 0) {
+                float *o_first = isS ? a.o + ((int64_t)e * a.w * a.n_chains + chain) * dk
+                                     : t.pvec + (((int64_t)req * t.max_list + j) * a.w * a.n_chains + chain) * dk;
+                seam_tokens<D, FAM>(X, sm, a.w, o_first, (int64_t)a.n_chains * dk, c0, c0, !isS, dk);
+            }
+        } else if (a.has_seam) {
             const int64_t sb = a.seam_begin[e];
             if (sb >= 0) {
                 for (int s0 = 0; s0 < a.w; s0 += SEAM_STAGE) {

@@ -271,6 +271,7 @@ template <int D, typename TIN>
 struct SeamPrefetch {
     using V4 = typename std::conditional<std::is_same<TIN, float>::value, f32x4, bf16x4>::type;
     V4 q, k, v;
+    V4 gv;  // per-channel log-gates (GLA)
     // gate and beta as raw bits in full registers (a bf16 sits in the low
     // half): 16-bit values packed into one register would be combined right
     // after the load, which waits for every load issued before them
@@ -324,6 +325,15 @@ __device__ __forceinline__ void seam_fetch(SeamPrefetch<D, TIN> &p, const Tok &x
     p.q = ld4(x.q);
     p.k = ld4(x.k);
     p.v = ld4(x.v);
+    if constexpr (fam_vgate(FAM)) {
+        const auto r = buffer_view(reinterpret_cast<const TIN *>(x.g) + (int64_t)chain * x.gcs + tb * x.gts,
+                                   on ? (int)(((int64_t)(nt - 1) * x.gts + dk) * sizeof(TIN)) : 0);
+        const int goff = (int)(((int64_t)t * x.gts + i) * sizeof(TIN));
+        if constexpr (std::is_same<TIN, float>::value)
+            p.gv = __builtin_bit_cast(V4, __builtin_amdgcn_raw_buffer_load_b128(r, goff, 0, 0));
+        else
+            p.gv = __builtin_bit_cast(V4, __builtin_amdgcn_raw_buffer_load_b64(r, goff, 0, 0));
+    }
     if (fam_sgate(FAM)) {
         const auto r = buffer_view(reinterpret_cast<const TIN *>(x.g) + (int64_t)chain * x.gcs + tb * x.gts,
                                    on ? (int)(((int64_t)(nt - 1) * x.gts + 1) * sizeof(TIN)) : 0);
@@ -404,9 +414,11 @@ __device__ __forceinline__ void seam_put_kda(SeamSmemKda<D> &sm, const KdaSeamPr
     if (tid < SEAM_STAGE) sm.beta[tid] = tid < nt ? scalar_from_bits<TIN>(p.b) : 1.f;
 }
 
-// Write a fetched stage into the LDS staging area (zero tokens past nt).
+// Write a fetched stage into the LDS staging area (zero tokens past nt); the
+// scalar decay is e^g (Mamba2, GDN), retnet_gamma (RetNet) or 1.
 template <int D, int FAM, typename TIN>
-__device__ __forceinline__ void seam_put(SeamSmem<D, FAM> &sm, const SeamPrefetch<D, TIN> &p, int dk, int nt) {
+__device__ __forceinline__ void seam_put(SeamSmem<D, FAM> &sm, const SeamPrefetch<D, TIN> &p, int dk, int nt,
+                                         float retnet_gamma = 1.f) {
     const int tid = threadIdx.x, t = tid / (D / 4), i = 4 * (tid % (D / 4));
     if (t >= SEAM_STAGE) return;  // (wave-uniform: whole waves past the stage's items)
     const bool ok = t < nt && i < dk;
@@ -420,8 +432,15 @@ __device__ __forceinline__ void seam_put(SeamSmem<D, FAM> &sm, const SeamPrefetc
     *reinterpret_cast<f32x4 *>(&sm.q[t][i]) = q4;
     *reinterpret_cast<f32x4 *>(&sm.k[t][i]) = k4;
     *reinterpret_cast<f32x4 *>(&sm.v[t][i]) = v4;
+    if constexpr (fam_vgate(FAM)) {
+        f32x4 a4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a4[e] = ok ? expf((float)p.gv[e]) : 1.f;
+        *reinterpret_cast<f32x4 *>(&sm.a[t][i]) = a4;
+    }
     if (i == 0) {
-        sm.a[t][0] = (fam_sgate(FAM) && t < nt) ? expf(scalar_from_bits<TIN>(p.g)) : 1.f;
+        if constexpr (!fam_vgate(FAM))
+            sm.a[t][0] = t >= nt ? 1.f : fam_sgate(FAM) ? expf(scalar_from_bits<TIN>(p.g)) : retnet_gamma;
         sm.beta[t] = (fam_beta(FAM) && t < nt) ? scalar_from_bits<TIN>(p.b) : 1.f;
     }
 }
