@@ -242,8 +242,10 @@ k_build_diag(BuildArgs a) {
 // factors are at most 1.  The staging lanes (one channel pair and one quarter
 // of the chunk's tokens each) write K~ = k * decay (hi and lo bf16) and V rows
 // to LDS; each wave then adds K~^T V into its 32 columns of the slice state on
-// the matrix cores, through transpose reads.  At the end the slice states are
-// combined through LDS; T = exp(sum of the segment's log-gates).
+// the matrix cores, through transpose reads.  A group's staging area is
+// double-buffered by chunk parity, so one barrier per chunk suffices and one
+// wave's staging overlaps another's products.  At the end the slice states
+// are combined through LDS; T = exp(sum of the segment's log-gates).
 template <int D>
 struct SliceCfg {
     static constexpr int NW = D / 32;  // waves per slice group (one per 32 columns / 32 channels)
@@ -258,7 +260,7 @@ struct SliceCfg {
     static constexpr int GRP = al(gV + CS * LDK * 2);
     static constexpr int LDS_ = D + 4;  // fp32 row stride of the combine's S
     static constexpr int cS = 0, cTot = al(D * LDS_ * 4);
-    static constexpr int total = (NG * GRP > cTot + NG * D * 4) ? NG * GRP : cTot + NG * D * 4;
+    static constexpr int total = (2 * NG * GRP > cTot + NG * D * 4) ? 2 * NG * GRP : cTot + NG * D * 4;
     static_assert(total <= 160 * 1024, "LDS budget");
 };
 
@@ -281,10 +283,8 @@ k_build_diag_slices(BuildArgs a) {
     const int64_t b0 = a.seg_begin[seg], n = a.seg_end[seg] - b0;
     const int nch = (int)((n + CS - 1) / CS);
     const int per = (nch + NG - 1) / NG;  // chunks per slice group
-    char *gb = smem + gi * Cfg::GRP;
-    bf16 *sK = reinterpret_cast<bf16 *>(gb + Cfg::gK);
-    bf16 *sKl = reinterpret_cast<bf16 *>(gb + Cfg::gKl);
-    bf16 *sV = reinterpret_cast<bf16 *>(gb + Cfg::gV);
+    // each group's staging area is double-buffered by chunk parity
+    char *gb0 = smem + 2 * gi * Cfg::GRP;
 
     // staging role: channels ch, ch + 1 and tokens 8 tq .. 8 tq + 7 of the chunk
     const int tq = lane >> 4, ch = 32 * q + 2 * (lane & 15);
@@ -329,6 +329,10 @@ k_build_diag_slices(BuildArgs a) {
     if (per > 0) fetch(first);
     for (int c = 0; c < per; ++c) {
         const int gc = first - c;
+        char *gb = gb0 + (c & 1) * Cfg::GRP;
+        bf16 *sK = reinterpret_cast<bf16 *>(gb + Cfg::gK);
+        bf16 *sKl = reinterpret_cast<bf16 *>(gb + Cfg::gKl);
+        bf16 *sV = reinterpret_cast<bf16 *>(gb + Cfg::gV);
         // ---- this lane's quarter: product of its 8 tokens' gates per channel
         auto gate = [&](int j, int e) -> float {
             if (!(pvalid & (1 << j))) return 0.f;
@@ -402,8 +406,10 @@ k_build_diag_slices(BuildArgs a) {
                 for (int nt = 0; nt < 2; ++nt) X[rt][nt] = mfma(kl, vb[nt], X[rt][nt]);
             }
         }
-        __syncthreads();
+        // (no barrier here: the next chunk stages into the other buffer, and a
+        // wave reaches the next barrier only after this carry)
     }
+    __syncthreads();  // every carry is done before the staging areas are reused
 
     // ---- combine the slice states in order through LDS
     float *cS = reinterpret_cast<float *>(smem + Cfg::cS);
