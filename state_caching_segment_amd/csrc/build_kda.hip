@@ -47,8 +47,8 @@ struct KdaCfg {
     static constexpr int al(int x) { return (x + 15) / 16 * 16; }
     static constexpr int offK = 0;                                   // raw keys, rows
     static constexpr int offKL = offK + al(KC * LDK * ES);           // K_L rows (split)
-    static constexpr int offVT = offKL + al(NS * KC * LDK * ES);     // V^T
-    static constexpr int offKtT = offVT + al(D * LDT * ES);          // Kt^T (split)
+    static constexpr int offVT = offKL + al(NS * KC * LDK * ES);     // V^T, two buffers by chunk parity
+    static constexpr int offKtT = offVT + 2 * al(D * LDT * ES);      // Kt^T (split)
     static constexpr int offG = offKtT + al(NS * D * LDT * ES);      // Gamma [t][i]
     static constexpr int offL = offG + al(KC * LDG * 4);
     static constexpr int offInv = offL + al(KC * LDL * 4);
@@ -139,7 +139,7 @@ k_build_kda(BuildArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[Cfg::total];
     OpT *sK = reinterpret_cast<OpT *>(smem + Cfg::offK);
     OpT *sKL = reinterpret_cast<OpT *>(smem + Cfg::offKL);
-    OpT *sVT = reinterpret_cast<OpT *>(smem + Cfg::offVT);
+    OpT *const sVT0 = reinterpret_cast<OpT *>(smem + Cfg::offVT);
     OpT *sKtT = reinterpret_cast<OpT *>(smem + Cfg::offKtT);
     float *sG = reinterpret_cast<float *>(smem + Cfg::offG);
     float *sL = reinterpret_cast<float *>(smem + Cfg::offL);
@@ -192,6 +192,7 @@ k_build_kda(BuildArgs a) {
     if (n > 0) prefetch(0);
 
     for (int64_t c0 = 0; c0 < n; c0 += KC) {
+        OpT *const sVT = sVT0 + (int)((c0 / KC) & 1) * (Cfg::al(D * LDT * Cfg::ES) / Cfg::ES);
         // ---- stage raw keys, V^T and log-gates
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -349,7 +350,10 @@ k_build_kda(BuildArgs a) {
                 for (int nt = 0; nt < 2; ++nt)
                     X[rt][nt] = mma_lds_perm<F32>(sKtT, LOT, LDT, 16 * rt + r16, 0, grp, rv[nt], X[rt][nt]);
         }
-        __syncthreads();
+        // (no barrier here: of what the next chunk's staging writes only V^T is
+        // read by the carry, and it alternates between two buffers; the rest is
+        // rewritten after the next chunk's first barrier, which every wave
+        // reaches only after this carry)
     }
 
     float *To = a.T + ((int64_t)seg * a.n_chains + chain) * dk * dk;
