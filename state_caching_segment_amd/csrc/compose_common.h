@@ -38,18 +38,60 @@ struct SeamSmemB {
 
 // A stage of KDA seam tokens in the decayed forms the chunk seam uses: with
 // E_t the window's cumulative per-channel decay through token t and E_c that
-// of its last token, rows E_t o q_t, E_t o k_t, k_t / E_t, (E_c / E_t) o k_t,
-// v_t, and E_c itself.  (Tokens past nt are zero tokens with decay 1.)
+// of its last token, rows E_t o k_t and E_t o q_t, k_t / E_t, (E_c / E_t) o k_t,
+// v_t, and E_c itself.  (Tokens past nt are zero tokens with decay 1.)  The
+// decayed rows are matrix-core operands, stored once already split into hi
+// and lo bf16 (so that no wave repeats the split): the row forms with the
+// channels of each 32-block in the permuted k order (kda_seam_pos), E_t o k_t
+// in rows 0-7 and E_t o q_t in rows 8-15 of lq; (E_c / E_t) o k_t transposed,
+// one 16-byte row of eight tokens per channel.
 template <int D>
-struct SeamSmemKda {
-    float ql[SEAM_STAGE][D];
-    float kl[SEAM_STAGE][D];
-    float kb[SEAM_STAGE][D];
-    float kt[SEAM_STAGE][D];
+struct __attribute__((aligned(16))) SeamSmemKda {
+    bf16 lqh[2 * SEAM_STAGE][D], lql[2 * SEAM_STAGE][D];
+    bf16 kbh[SEAM_STAGE][D], kbl[SEAM_STAGE][D];
+    bf16 kth[D][SEAM_STAGE], ktl[D][SEAM_STAGE];
     float v[SEAM_STAGE][D];
     float ecl[D];
     float beta[SEAM_STAGE];
 };
+
+// Position of channel i in a permuted row: within each 32-block, lane group g
+// reads positions 8g .. 8g+7, which hold channels 4g .. 4g+3 and
+// 16+4g .. 16+4g+3 (the permuted k subset of the matrix-core convention).
+__device__ __forceinline__ int kda_seam_pos(int i) {
+    const int c = i & 31;
+    return (i & ~31) + 8 * ((c & 15) >> 2) + 4 * (c >> 4) + (c & 3);
+}
+
+// Channel i's column of a KDA seam stage, from its window values (zeroed past
+// nt), cumulative decays e[t] = E_t and E_c = pr.
+template <int D>
+__device__ __forceinline__ void kda_stage_write(SeamSmemKda<D> &sm, int i, const float (&qv)[SEAM_STAGE],
+                                                const float (&kv)[SEAM_STAGE], const float (&vv)[SEAM_STAGE],
+                                                const float (&e)[SEAM_STAGE], float pr) {
+    const int pi = kda_seam_pos(i);
+    bf16x8 th, tl;
+#pragma unroll
+    for (int t = 0; t < SEAM_STAGE; ++t) {
+        bf16 h, l;
+        split1(e[t] * kv[t], h, l);
+        sm.lqh[t][pi] = h;
+        sm.lql[t][pi] = l;
+        split1(e[t] * qv[t], h, l);
+        sm.lqh[SEAM_STAGE + t][pi] = h;
+        sm.lql[SEAM_STAGE + t][pi] = l;
+        split1(kv[t] / e[t], h, l);
+        sm.kbh[t][pi] = h;
+        sm.kbl[t][pi] = l;
+        split1(kv[t] * (pr / e[t]), h, l);
+        th[t] = h;
+        tl[t] = l;
+        sm.v[t][i] = vv[t];
+    }
+    *reinterpret_cast<bf16x8 *>(&sm.kth[i][0]) = th;
+    *reinterpret_cast<bf16x8 *>(&sm.ktl[i][0]) = tl;
+    sm.ecl[i] = pr;
+}
 
 template <int D, typename TIN>
 __device__ void stage_seam_kda(SeamSmemKda<D> &sm, const Tok &x, int chain, int dk, int64_t tok0, int nt) {
@@ -79,15 +121,7 @@ __device__ void stage_seam_kda(SeamSmemKda<D> &sm, const Tok &x, int chain, int 
             e[t] = p;
             if (!ok) qv[t] = kv[t] = vv[t] = 0.f;
         }
-#pragma unroll
-        for (int t = 0; t < SEAM_STAGE; ++t) {
-            sm.ql[t][i] = e[t] * qv[t];
-            sm.kl[t][i] = e[t] * kv[t];
-            sm.kb[t][i] = kv[t] / e[t];
-            sm.kt[t][i] = kv[t] * (p / e[t]);
-            sm.v[t][i] = vv[t];
-        }
-        sm.ecl[i] = p;
+        kda_stage_write<D>(sm, i, qv, kv, vv, e, p);
     }
     if (tid < SEAM_STAGE) {
         const int t = tid;
@@ -401,15 +435,7 @@ __device__ __forceinline__ void seam_put_kda(SeamSmemKda<D> &sm, const KdaSeamPr
             kv[t] = ok ? scalar_from_bits<TIN>(p.k[t]) : 0.f;
             vv[t] = ok ? scalar_from_bits<TIN>(p.v[t]) : 0.f;
         }
-#pragma unroll
-        for (int t = 0; t < SEAM_STAGE; ++t) {
-            sm.ql[t][i] = e[t] * qv[t];
-            sm.kl[t][i] = e[t] * kv[t];
-            sm.kb[t][i] = kv[t] / e[t];
-            sm.kt[t][i] = kv[t] * (pr / e[t]);
-            sm.v[t][i] = vv[t];
-        }
-        sm.ecl[i] = pr;
+        kda_stage_write<D>(sm, i, qv, kv, vv, e, pr);
     }
     if (tid < SEAM_STAGE) sm.beta[tid] = tid < nt ? scalar_from_bits<TIN>(p.b) : 1.f;
 }
@@ -699,25 +725,15 @@ __device__ void seam_chunk_kda(f32x4 (&X)[D / 16][2], const SeamSmemKda<D> &sm, 
     const int lane = lane_fresh(), r16 = lane & 15, grp = lane >> 4;
     const int tr = r16 & (SEAM_STAGE - 1);  // this lane's token row
     // [E o K; E o Q] rows (A operand of P and of the Gram) and (K / E) rows
-    // (B operand of the Gram, zero in columns 8-15), split, per k block
+    // (B operand of the Gram: columns 8-15 of the Gram repeat 0-7 and are
+    // never read), staged split, per k block
     bf16x8 lh[KB], ll[KB], bh[KB], bl[KB];
-    const float *lrow = r16 < 8 ? &sm.kl[tr][0] : &sm.ql[tr][0];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-        float av[8], bv[8];
-        const f32x4 a0 = *reinterpret_cast<const f32x4 *>(lrow + 32 * kb + 4 * grp);
-        const f32x4 a1 = *reinterpret_cast<const f32x4 *>(lrow + 32 * kb + 16 + 4 * grp);
-        const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&sm.kb[tr][32 * kb + 4 * grp]);
-        const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&sm.kb[tr][32 * kb + 16 + 4 * grp]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            av[e] = a0[e];
-            av[4 + e] = a1[e];
-            bv[e] = r16 < 8 ? b0[e] : 0.f;
-            bv[4 + e] = r16 < 8 ? b1[e] : 0.f;
-        }
-        split8(av, lh[kb], ll[kb]);
-        split8(bv, bh[kb], bl[kb]);
+        lh[kb] = *reinterpret_cast<const bf16x8 *>(&sm.lqh[r16][32 * kb + 8 * grp]);
+        ll[kb] = *reinterpret_cast<const bf16x8 *>(&sm.lql[r16][32 * kb + 8 * grp]);
+        bh[kb] = *reinterpret_cast<const bf16x8 *>(&sm.kbh[tr][32 * kb + 8 * grp]);
+        bl[kb] = *reinterpret_cast<const bf16x8 *>(&sm.kbl[tr][32 * kb + 8 * grp]);
     }
     // P = [E o K; E o Q] S0 and the Gram [E o K; E o Q] (K / E)^T
     f32x4 P[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -781,13 +797,10 @@ __device__ void seam_chunk_kda(f32x4 (&X)[D / 16][2], const SeamSmemKda<D> &sm, 
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int ch = 16 * rt + r16;
-        f32x4 kt;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float v = sm.kt[r0 + e][ch];
-            kt[e] = grp < 2 ? v : 0.f;
-        }
-        split4v(kt, kth[rt], ktl[rt]);
+        const s4v h = *reinterpret_cast<const s4v *>(&sm.kth[ch][r0]);
+        const s4v l = *reinterpret_cast<const s4v *>(&sm.ktl[ch][r0]);
+        kth[rt] = grp < 2 ? h : s4v{0, 0, 0, 0};
+        ktl[rt] = grp < 2 ? l : s4v{0, 0, 0, 0};
         ecr[rt] = *reinterpret_cast<const f32x4 *>(&sm.ecl[16 * rt + 4 * grp]);
     }
 #pragma unroll
