@@ -302,7 +302,7 @@ k_compose_dense(TreeArgs t) {
     if (m > 0) {
         win_load(0);
         t_load(0);
-        s_load(0);
+        if (!TREE || F32) s_load(0);
         t_put(0);
         t_load(m > 1 ? 1 : 0);
         if (seam_one_stage) seam_fetch<D, FAM, TIN>(seam_pf, a.x, chain, dk, sb_at(0), a.w);
@@ -348,7 +348,10 @@ k_compose_dense(TreeArgs t) {
             }
         }
         // S <- T_j S + S_j; the next S_j is requested as soon as this one is in
-        // the accumulators
+        // the accumulators.  Tree mode (bf16) instead loads S_j in the S half
+        // only, just before the product, and adds it after the product: no
+        // S_j registers are held across the seam window, where its eight
+        // waves run out of registers
         if (F32) {
             float xv[KB][2][8];
 #pragma unroll
@@ -392,12 +395,11 @@ k_compose_dense(TreeArgs t) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    const f32x4 sj = quad_transpose(spre[rt][nt], lane);
-                    X[rt][nt] = isS ? sj : f32x4{0.f, 0.f, 0.f, 0.f};
-                }
+                for (int nt = 0; nt < 2; ++nt)
+                    X[rt][nt] = (!TREE && isS) ? quad_transpose(spre[rt][nt], lane) : f32x4{0.f, 0.f, 0.f, 0.f};
             const int jn = j + 1 < m ? j + 1 : j;
-            s_load(jn);
+            if (!TREE) s_load(jn);
+            else if (isS) s_load(j);
             if (seam_one_stage) seam_fetch<D, FAM, TIN>(seam_pf, a.x, chain, dk, sb_at(jn), a.w);
             if constexpr (KDA_PF)
                 if (kda_one_stage) seam_fetch_kda<D, TIN>(kda_pf, a.x, chain, dk, sb_at(jn), a.w);
@@ -416,6 +418,12 @@ k_compose_dense(TreeArgs t) {
                         X[rt][nt] = mfma(al, xh[kb][nt], X[rt][nt]);
                     }
                 }
+            if (TREE && isS) {
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) X[rt][nt] += quad_transpose(spre[rt][nt], lane);
+            }
         }
         if (j + 1 < m) t_put((j + 1) & 1);  // that buffer's last readers finished entry j - 1
         t_load(j + 2 < m ? j + 2 : m - 1);
