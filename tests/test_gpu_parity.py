@@ -60,7 +60,9 @@ def test_kda(dtype, d):
 
 @pytest.mark.parametrize("fam,dtype,d", [("gdn", "bf16", 128), ("kda", "bf16", 128), ("gla", "bf16", 64),
                                          ("gla", "bf16", 128), ("retnet", "f32", 32), ("retnet", "bf16", 16),
-                                         ("deltanet", "f32", 16), ("mamba2", "bf16", 64), ("linear", "f32", 64)])
+                                         ("deltanet", "f32", 16), ("mamba2", "bf16", 64), ("linear", "f32", 64),
+                                         ("deltanet", "bf16", 128), ("kda", "bf16", 64), ("kda", "bf16", 16),
+                                         ("gdn", "bf16", 32)])
 def test_tree_compose(fam, dtype, d):
     """Tree-scan compose (several requests of unequal length, lists not a
     multiple of the block size) against the oracle's left-to-right path."""
