@@ -283,7 +283,10 @@ k_compose_dense(TreeArgs t) {
     // too, one channel per thread, and staged in its decayed forms at the
     // seam (in tree mode, eight waves at 256 registers, it would spill)
     constexpr bool KDA_PF = CHUNK_SEAM && FAM == KDA && !TREE;
-    KdaSeamPrefetch<D, TIN> kda_pf;
+    // (a prefetched window is staged by KNG threads per channel: every
+    // thread of the workgroup)
+    constexpr int KNG = NWT * 64 / D;
+    KdaSeamPrefetch<D, TIN, KNG> kda_pf;
     const bool kda_one_stage = KDA_PF && a.has_seam && a.w <= SEAM_STAGE;
 
     f32x4 X[RT][2];
@@ -307,7 +310,7 @@ k_compose_dense(TreeArgs t) {
         t_load(m > 1 ? 1 : 0);
         if (seam_one_stage) seam_fetch<D, FAM, TIN>(seam_pf, a.x, chain, dk, sb_at(0), a.w);
         if constexpr (KDA_PF)
-            if (kda_one_stage) seam_fetch_kda<D, TIN>(kda_pf, a.x, chain, dk, sb_at(0), a.w);
+            if (kda_one_stage) seam_fetch_kda<D, TIN, KNG>(kda_pf, a.x, chain, dk, sb_at(0), a.w);
         __syncthreads();
     }
     for (int j = 0; j < m; ++j) {
@@ -328,7 +331,7 @@ k_compose_dense(TreeArgs t) {
             } else if (sb >= 0 && kda_one_stage) {
                 if constexpr (KDA_PF) {
                     __syncthreads();
-                    seam_put_kda<D, TIN>(sm, kda_pf, dk, a.w);
+                    seam_put_kda<D, TIN, KNG>(sm, kda_pf, dk, a.w);
                     __syncthreads();
                     seam_stage_run<D, FAM, CHUNK_SEAM>(X, sm, a.w, seam_out(t, isS, e, req, j0 + j, chain, 0, dk), a,
                                                        c0, dk, seam_nm[wv], !isS);
@@ -371,7 +374,7 @@ k_compose_dense(TreeArgs t) {
             s_load(jn);
             if (seam_one_stage) seam_fetch<D, FAM, TIN>(seam_pf, a.x, chain, dk, sb_at(jn), a.w);
             if constexpr (KDA_PF)
-                if (kda_one_stage) seam_fetch_kda<D, TIN>(kda_pf, a.x, chain, dk, sb_at(jn), a.w);
+                if (kda_one_stage) seam_fetch_kda<D, TIN, KNG>(kda_pf, a.x, chain, dk, sb_at(jn), a.w);
             const float *tf = reinterpret_cast<const float *>(tsm[j & 1]);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
@@ -402,7 +405,7 @@ k_compose_dense(TreeArgs t) {
             else if (isS) s_load(j);
             if (seam_one_stage) seam_fetch<D, FAM, TIN>(seam_pf, a.x, chain, dk, sb_at(jn), a.w);
             if constexpr (KDA_PF)
-                if (kda_one_stage) seam_fetch_kda<D, TIN>(kda_pf, a.x, chain, dk, sb_at(jn), a.w);
+                if (kda_one_stage) seam_fetch_kda<D, TIN, KNG>(kda_pf, a.x, chain, dk, sb_at(jn), a.w);
             const bf16 *th = reinterpret_cast<const bf16 *>(tsm[j & 1]);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)

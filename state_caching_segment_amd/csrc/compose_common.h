@@ -63,6 +63,49 @@ __device__ __forceinline__ int kda_seam_pos(int i) {
     return (i & ~31) + 8 * ((c & 15) >> 2) + 4 * (c >> 4) + (c & 3);
 }
 
+// Token t of channel i of a KDA seam stage, from its values (zero past nt),
+// its cumulative decay et = E_t and the window's E_c = pr.
+template <int D>
+__device__ __forceinline__ void kda_stage_tok(SeamSmemKda<D> &sm, int i, int t, float qv, float kv, float vv, float et,
+                                              float pr) {
+    const int pi = kda_seam_pos(i);
+    bf16 h, l;
+    split1(et * kv, h, l);
+    sm.lqh[t][pi] = h;
+    sm.lql[t][pi] = l;
+    split1(et * qv, h, l);
+    sm.lqh[SEAM_STAGE + t][pi] = h;
+    sm.lql[SEAM_STAGE + t][pi] = l;
+    split1(kv / et, h, l);
+    sm.kbh[t][pi] = h;
+    sm.kbl[t][pi] = l;
+    split1(kv * (pr / et), h, l);
+    sm.kth[i][t] = h;
+    sm.ktl[i][t] = l;
+    sm.v[t][i] = vv;
+}
+
+// Cumulative decays of channel i over the window from its log-gates (e^g as
+// 2^(g log2 e)); tokens past nt and padded channels decay by 1.  Returns E_c.
+__device__ __forceinline__ float kda_window_decay(const float (&gv)[SEAM_STAGE], int i, int dk, int nt,
+                                                  float (&e)[SEAM_STAGE]) {
+    float p = 1.f;
+#pragma unroll
+    for (int t = 0; t < SEAM_STAGE; ++t) {
+        p *= (t < nt && i < dk) ? __builtin_amdgcn_exp2f(gv[t] * 1.4426950408889634f) : 1.f;
+        e[t] = p;
+    }
+    return p;
+}
+
+// e[t] for a token index known only at run time (no dynamic register index).
+__device__ __forceinline__ float kda_pick(const float (&e)[SEAM_STAGE], int t) {
+    float r = e[0];
+#pragma unroll
+    for (int s = 1; s < SEAM_STAGE; ++s) r = t == s ? e[s] : r;
+    return r;
+}
+
 // Channel i's column of a KDA seam stage, from its window values (zeroed past
 // nt), cumulative decays e[t] = E_t and E_c = pr.
 template <int D>
@@ -385,16 +428,22 @@ __device__ __forceinline__ void seam_fetch(SeamPrefetch<D, TIN> &p, const Tok &x
 // product needs), as raw bits; threads past d repeat loads and write nothing.
 // When the entry has no seam (tok0 < 0) every view is empty and the values
 // read as zero; so do tokens past nt.
-template <int D, typename TIN>
+// A KDA seam window fetched ahead into registers, spread over NG threads per
+// channel (the launch has NG * d threads): thread (group gq, channel i) holds
+// every gate of channel i and the q, k, v of tokens gq * SEAM_STAGE / NG
+// onwards.
+template <int D, typename TIN, int NG>
 struct KdaSeamPrefetch {
-    uint32_t q[SEAM_STAGE], k[SEAM_STAGE], v[SEAM_STAGE], g[SEAM_STAGE];
+    uint32_t g[SEAM_STAGE];
+    uint32_t q[SEAM_STAGE / NG], k[SEAM_STAGE / NG], v[SEAM_STAGE / NG];
     uint32_t b;  // beta of token tid (threads tid < SEAM_STAGE)
 };
 
-template <int D, typename TIN>
-__device__ __forceinline__ void seam_fetch_kda(KdaSeamPrefetch<D, TIN> &p, const Tok &x, int chain, int dk,
+template <int D, typename TIN, int NG>
+__device__ __forceinline__ void seam_fetch_kda(KdaSeamPrefetch<D, TIN, NG> &p, const Tok &x, int chain, int dk,
                                                int64_t tok0, int nt) {
-    const int tid = threadIdx.x, i = tid % D, ic = i < dk ? i : dk - 1;
+    constexpr int TPG = SEAM_STAGE / NG;
+    const int tid = threadIdx.x, i = tid % D, t0 = NG == 1 ? 0 : tid / D * TPG, ic = i < dk ? i : dk - 1;
     const bool on = tok0 >= 0;
     const int64_t tb = on ? tok0 : 0;
     const int rb = on ? (int)(((int64_t)(nt - 1) * x.ts + dk) * sizeof(TIN)) : 0;
@@ -405,12 +454,14 @@ __device__ __forceinline__ void seam_fetch_kda(KdaSeamPrefetch<D, TIN> &p, const
     const auto rv = buffer_view(reinterpret_cast<const TIN *>(x.v) + base, rb);
     const auto rg = buffer_view(reinterpret_cast<const TIN *>(x.g) + (int64_t)chain * x.gcs + tb * x.gts, gb);
 #pragma unroll
-    for (int t = 0; t < SEAM_STAGE; ++t) {
-        const int off = (int)(((int64_t)t * x.ts + ic) * sizeof(TIN));
-        p.q[t] = buffer_scalar_bits<TIN>(rq, off);
-        p.k[t] = buffer_scalar_bits<TIN>(rk, off);
-        p.v[t] = buffer_scalar_bits<TIN>(rv, off);
+    for (int t = 0; t < SEAM_STAGE; ++t)
         p.g[t] = buffer_scalar_bits<TIN>(rg, (int)(((int64_t)t * x.gts + ic) * sizeof(TIN)));
+#pragma unroll
+    for (int u = 0; u < TPG; ++u) {
+        const int off = (int)(((int64_t)(t0 + u) * x.ts + ic) * sizeof(TIN));
+        p.q[u] = buffer_scalar_bits<TIN>(rq, off);
+        p.k[u] = buffer_scalar_bits<TIN>(rk, off);
+        p.v[u] = buffer_scalar_bits<TIN>(rv, off);
     }
     const int tt = tid % SEAM_STAGE;
     const auto rbeta = buffer_view(reinterpret_cast<const TIN *>(x.beta) + (int64_t)chain * x.bcs + tb * x.bts,
@@ -419,23 +470,28 @@ __device__ __forceinline__ void seam_fetch_kda(KdaSeamPrefetch<D, TIN> &p, const
 }
 
 // Stage a fetched KDA seam window in the decayed forms (the arithmetic of
-// stage_seam_kda, from registers).
-template <int D, typename TIN>
-__device__ __forceinline__ void seam_put_kda(SeamSmemKda<D> &sm, const KdaSeamPrefetch<D, TIN> &p, int dk, int nt) {
+// stage_seam_kda, from registers): each thread forms its channel's cumulative
+// decays from all the gates and writes its group's tokens.
+template <int D, typename TIN, int NG>
+__device__ __forceinline__ void seam_put_kda(SeamSmemKda<D> &sm, const KdaSeamPrefetch<D, TIN, NG> &p, int dk,
+                                             int nt) {
+    constexpr int TPG = SEAM_STAGE / NG;
     const int tid = threadIdx.x;
-    if (tid < D) {
-        const int i = tid;
-        float qv[SEAM_STAGE], kv[SEAM_STAGE], vv[SEAM_STAGE], e[SEAM_STAGE], pr = 1.f;
+    if (tid < NG * D) {
+        const int i = tid % D, t0 = NG == 1 ? 0 : tid / D * TPG;
+        float gv[SEAM_STAGE], e[SEAM_STAGE];
 #pragma unroll
-        for (int t = 0; t < SEAM_STAGE; ++t) {
+        for (int t = 0; t < SEAM_STAGE; ++t) gv[t] = scalar_from_bits<TIN>(p.g[t]);
+        const float pr = kda_window_decay(gv, i, dk, nt, e);
+#pragma unroll
+        for (int u = 0; u < TPG; ++u) {
+            const int t = t0 + u;
             const bool ok = t < nt && i < dk;
-            pr *= ok ? __builtin_amdgcn_exp2f(scalar_from_bits<TIN>(p.g[t]) * 1.4426950408889634f) : 1.f;
-            e[t] = pr;
-            qv[t] = ok ? scalar_from_bits<TIN>(p.q[t]) : 0.f;
-            kv[t] = ok ? scalar_from_bits<TIN>(p.k[t]) : 0.f;
-            vv[t] = ok ? scalar_from_bits<TIN>(p.v[t]) : 0.f;
+            kda_stage_tok<D>(sm, i, t, ok ? scalar_from_bits<TIN>(p.q[u]) : 0.f,
+                             ok ? scalar_from_bits<TIN>(p.k[u]) : 0.f, ok ? scalar_from_bits<TIN>(p.v[u]) : 0.f,
+                             kda_pick(e, t), pr);
         }
-        kda_stage_write<D>(sm, i, qv, kv, vv, e, pr);
+        if (t0 == 0) sm.ecl[i] = pr;
     }
     if (tid < SEAM_STAGE) sm.beta[tid] = tid < nt ? scalar_from_bits<TIN>(p.b) : 1.f;
 }
