@@ -122,11 +122,20 @@ int64_t hypic_t_elems(int32_t family, int32_t dk) {
 
 namespace {
 
-// Tree-mode blocking: about sqrt(list length) entries per block.
-int tree_block(int max_list) {
+// Tree-mode blocking.  About sqrt(list length) entries per block gives the
+// most parallel work.  Where the chains alone (n_req x n_chains) give more
+// than enough, fewer and longer blocks are taken (less aggregate traffic, scan
+// and fix-up work), as long as at least 8 block workgroups remain per compute
+// unit of the MI355X (256).  Blocks are then evened out, at most 64 entries.
+int tree_block(int max_list, int64_t chains) {
+    if (max_list <= 0) return 1;
     int b = 1;
     while (b * b < max_list) ++b;
-    return b < 1 ? 1 : (b > 64 ? 64 : b);
+    int nb = (max_list + b - 1) / b;
+    constexpr int64_t kMinBlockGroups = 8 * 256;
+    while (nb > 1 && chains * (nb - 1) >= kMinBlockGroups) --nb;
+    b = (max_list + nb - 1) / nb;
+    return b > 64 ? 64 : b;
 }
 
 struct TreeLayout {
@@ -136,7 +145,7 @@ struct TreeLayout {
 
 TreeLayout tree_layout(const hypic_layout *L, int n_req, int max_list, int w) {
     TreeLayout t;
-    t.B = tree_block(max_list);
+    t.B = tree_block(max_list, (int64_t)n_req * L->n_chains);
     t.NB = max_list > 0 ? (max_list + t.B - 1) / t.B : 0;
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
     const size_t agg = (size_t)n_req * t.NB * L->n_chains * L->dk * L->dk * sizeof(float);

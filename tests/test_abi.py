@@ -117,6 +117,12 @@ def test_workspace_query():
     assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 4, 48, 0) == 3 * agg
     assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 4, 48, -1) == 0
     assert hy.hypic_workspace_bytes(hy.layout("gdn", "bf16", 4, 100), hy.OP_COMPOSE_TREE, 4, 48, 8) == 0
+    # 16 requests x 32 chains (one KDA layer) of 128 entries: the chains fill the GPU, so 4 blocks
+    # of 32 entries (8 block workgroups per compute unit) instead of 11 blocks of 12
+    L = hy.layout("kda", "bf16", 32, 128)
+    agg = 16 * 4 * 32 * 128 * 128 * 4
+    pv = 16 * 128 * 8 * 32 * 128 * 4
+    assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 16, 128, 8) == 3 * agg + pv
 
 
 def test_request_plan():
