@@ -156,10 +156,10 @@ int hypic_segment_build(const hypic_layout *L, const hypic_tokens *x, int32_t n_
  *   d_o           [n_entries][w][n_chains][dv]; rows of entries without a seam
  *                 are left untouched.  May be NULL when seam == NULL.
  * mode HYPIC_TREE computes the same result (to rounding) through the
- * associative scan: blocks of about sqrt(max_list_len) entries (fewer, longer
- * blocks, at most 64 entries, when n_req * n_chains alone fill the GPU) are
- * reduced in parallel, their aggregates scanned, and seam outputs fixed up; it
- * needs a
+ * associative scan: blocks of about sqrt(max_list_len) entries (shorter ones
+ * when the blocks cannot fill the GPU; fewer, longer ones, at most 64
+ * entries, when n_req * n_chains alone fill it) are reduced in parallel,
+ * their aggregates scanned, and seam outputs fixed up; it needs a
  * workspace of hypic_workspace_bytes(L, HYPIC_OP_COMPOSE_TREE, n_req,
  * max_list_len, w) bytes (HYPIC_E_WORKSPACE if missing or smaller).  HYPIC_SEQ
  * needs none.  max_list_len must bound every request's entry count.

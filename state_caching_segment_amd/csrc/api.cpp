@@ -122,18 +122,29 @@ int64_t hypic_t_elems(int32_t family, int32_t dk) {
 
 namespace {
 
-// Tree-mode blocking.  About sqrt(list length) entries per block gives the
-// most parallel work.  Where the chains alone (n_req x n_chains) give more
-// than enough, fewer and longer blocks are taken (less aggregate traffic, scan
-// and fix-up work), as long as at least 8 block workgroups remain per compute
-// unit of the MI355X (256).  Blocks are then evened out, at most 64 entries.
+// Tree-mode blocking, for the MI355X's 256 compute units.  About sqrt(m)
+// entries per block (m = list length) balances the parallel block phase
+// against the sequential scan over block aggregates.  Two cases shift it:
+// - Too few block workgroups to fill the GPU: blocks of about sqrt(m / 2)
+//   entries.  A block entry costs more than a scan step, so this pays until
+//   the scan grows long.
+// - The chains alone (n_req x n_chains) give surplus parallelism: fewer,
+//   longer blocks (less aggregate traffic, scan and fix-up work), as long as
+//   at least 8 block workgroups remain per compute unit.
+// Blocks are then evened out, at most 64 entries.
 int tree_block(int max_list, int64_t chains) {
     if (max_list <= 0) return 1;
+    constexpr int64_t kCUs = 256;
     int b = 1;
     while (b * b < max_list) ++b;
     int nb = (max_list + b - 1) / b;
-    constexpr int64_t kMinBlockGroups = 8 * 256;
-    while (nb > 1 && chains * (nb - 1) >= kMinBlockGroups) --nb;
+    if (chains * nb < kCUs) {
+        b = 1;
+        while (2 * b * b < max_list) ++b;
+        nb = (max_list + b - 1) / b;
+    } else {
+        while (nb > 1 && chains * (nb - 1) >= 8 * kCUs) --nb;
+    }
     b = (max_list + nb - 1) / nb;
     return b > 64 ? 64 : b;
 }

@@ -110,8 +110,9 @@ def test_workspace_query():
     L = hy.layout("gdn", "bf16", 4, 128)
     assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_SEQ, 4, 48, 8) == 0
     assert hy.hypic_workspace_bytes(L, hy.OP_BUILD, 4, 48, 8) == 0
-    # tree: 3 block-aggregate arrays of n_req x ceil(48/7) x chains x dk^2 fp32, plus seam queries
-    nb, agg = 7, 4 * 7 * 4 * 128 * 128 * 4
+    # tree: 3 block-aggregate arrays of n_req x NB x chains x dk^2 fp32, plus seam queries; 16 chains
+    # cannot fill the GPU, so blocks of ceil(sqrt(48 / 2)) = 5 entries, NB = 10
+    nb, agg = 10, 4 * 10 * 4 * 128 * 128 * 4
     pv = 4 * 48 * 8 * 4 * 128 * 4
     assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 4, 48, 8) == 3 * agg + pv
     assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 4, 48, 0) == 3 * agg
