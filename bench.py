@@ -229,8 +229,8 @@ def main():
     hits = not cold.all()
     if args.compose == "auto":
         n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
-        # the tree's parallel blocks pay only on long lists: C3's 32 entries on 16
-        # chains (0.24 ms against 0.44), not C2's 8 entries on 8 chains
+        # the tree's parallel blocks pay only on long lists: 32 entries on 16 GLA
+        # chains (0.20 ms against 0.44), not 8 entries on 8 chains
         mode = hy.TREE if hits or (plan.n_req * C < n_cu and plan.max_list_len >= 16) else hy.SEQ
     else:
         mode = hy.TREE if args.compose == "tree" else hy.SEQ
