@@ -124,6 +124,13 @@ def test_workspace_query():
     agg = 16 * 4 * 32 * 128 * 128 * 4
     pv = 16 * 128 * 8 * 32 * 128 * 4
     assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 16, 128, 8) == 3 * agg + pv
+    # one request of 32 entries on 16 GLA chains: 16 x 6 blocks cannot fill the GPU, so blocks of
+    # ceil(sqrt(32 / 2)) = 4 entries, NB = 8 (GLA's aggregates are still dk x dk fp32 states)
+    L = hy.layout("gla", "bf16", 16, 128)
+    assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 1, 32, 0) == 3 * (1 * 8 * 16 * 128 * 128 * 4)
+    # 5000 entries on 512 chains: longer blocks are capped at 64 entries, NB = ceil(5000 / 64) = 79
+    L = hy.layout("gdn", "bf16", 32, 64)
+    assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 16, 5000, 0) == 3 * (16 * 79 * 32 * 64 * 64 * 4)
 
 
 def test_request_plan():
