@@ -229,9 +229,10 @@ def main():
     hits = not cold.all()
     if args.compose == "auto":
         n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
-        # the tree's parallel blocks pay only on long lists: 32 entries on 16 GLA
-        # chains (0.20 ms against 0.44), not 8 entries on 8 chains
-        mode = hy.TREE if hits or (plan.n_req * C < n_cu and plan.max_list_len >= 16) else hy.SEQ
+        # with too few chains to fill the GPU the tree's parallel blocks pay
+        # from lists of 8 entries: 32 entries on 16 GLA chains (0.20 ms against
+        # 0.44), 8 entries on 8 RetNet chains (0.042 ms against 0.048)
+        mode = hy.TREE if hits or (plan.n_req * C < n_cu and plan.max_list_len >= 8) else hy.SEQ
     else:
         mode = hy.TREE if args.compose == "tree" else hy.SEQ
     if hits:
