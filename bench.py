@@ -261,7 +261,8 @@ def main():
         if ev:
             ev[2].record(stream)
         hy.hypic_compose(L, cmode, plan.n_req, plan.max_list_len, lo, pid, plan.n_slots, T, S, x, seam, w, state,
-                         o, ws if cmode == hy.TREE else None, nws if cmode == hy.TREE else 0, stream=stream)
+                         o, ws=ws if cmode == hy.TREE else None, ws_bytes=nws if cmode == hy.TREE else 0,
+                         stream=stream)
         if ev:
             ev[3].record(stream)
 

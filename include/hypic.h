@@ -46,12 +46,25 @@
  *     thread-safe.
  *   - Errors: arguments visible on the host are validated before any HIP
  *     call (null pointers, unknown family/dtype, dims, w, strides and 16-byte
- *     alignment of q/k/v rows, workspace size).  A failing check returns a
- *     negative status and enqueues nothing.  Launch failures return
- *     HYPIC_E_DEVICE.  Device-resident contents (offsets, slot ids) are
- *     trusted; out-of-range values there are undefined behaviour.  The detail
- *     of the last error on the calling thread is in hypic_last_error().
- *     On error the outputs are unspecified.
+ *     alignment of q/k/v rows, token strides up to 2^24 elements, workspace
+ *     size).  A failing check returns a negative status and enqueues nothing.
+ *     Launch failures return HYPIC_E_DEVICE.  Device-resident contents
+ *     (offsets, slot ids) are trusted; out-of-range values there are
+ *     undefined behaviour -- unless the environment variable HYPIC_VALIDATE
+ *     is "1": then every call first reads them back (a synchronous copy on
+ *     `stream`) and rejects, with HYPIC_E_INVALID, segment ranges that are
+ *     negative, reversed or longer than max_seg_len; list offsets that are
+ *     negative, decreasing or longer than max_list_len; slot ids outside
+ *     [0, n_slots); seam starts below -1; negative seam-advance starts.  The
+ *     token count is not an argument, so token indices are checked for sign
+ *     only.  The detail of the last error on the calling thread is in
+ *     hypic_last_error().  On error the outputs are unspecified.
+ *   - HYPIC_FAULT_INJECT ("1" or "all"; or "build", "compose", "seam" for one
+ *     call): after its arguments have been validated, the call returns
+ *     HYPIC_E_DEVICE and enqueues nothing.  For testing callers' error paths.
+ *   - dv must equal dk (HYPIC_E_UNSUPPORTED otherwise): every kernel keeps the
+ *     state and T in tiles of the same width, and every workload these
+ *     kernels are sized for has dk == dv.
  */
 #ifndef HYPIC_H
 #define HYPIC_H
@@ -155,6 +168,13 @@ int hypic_segment_build(const hypic_layout *L, const hypic_tokens *x, int32_t n_
  *                 fresh request), out = final state
  *   d_o           [n_entries][w][n_chains][dv]; rows of entries without a seam
  *                 are left untouched.  May be NULL when seam == NULL.
+ *   d_prefix_states  NULL, or [n_entries][n_chains][dk][dv]: the state after
+ *                 entry e (its seam window and its pair), for every entry e
+ *                 the lists name (the running states a combine step hands on;
+ *                 codernav.top, segment parallelism).  Indexed like d_pair_id.
+ *                 In HYPIC_TREE mode they come from a second, parallel pass
+ *                 over each block from the state entering it (the scan's
+ *                 down-sweep), which also writes the block's seam outputs.
  * mode HYPIC_TREE computes the same result (to rounding) through the
  * associative scan: blocks of about sqrt(max_list_len) entries (shorter ones
  * when the blocks cannot fill the GPU; fewer, longer ones, at most 64
@@ -168,7 +188,7 @@ int hypic_compose(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t ma
                   const int32_t *d_list_off, const int32_t *d_pair_id, int64_t n_slots,
                   const float *d_T, const float *d_S, const hypic_tokens *seam,
                   const int64_t *d_seam_begin, int32_t w, float *d_state, float *d_o,
-                  void *d_ws, size_t ws_bytes, void *stream);
+                  float *d_prefix_states, void *d_ws, size_t ws_bytes, void *stream);
 
 /*
  * hypic_seam_advance -- advance n_items independent states through w tokens

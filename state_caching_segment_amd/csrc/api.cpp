@@ -5,7 +5,10 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <string>
+#include <vector>
 
 #include "../../include/hypic.h"
 #include "kernels.h"
@@ -28,6 +31,8 @@ int ok() {
     g_last_error.clear();
     return HYPIC_OK;
 }
+
+constexpr int64_t kMaxTokStride = int64_t(1) << 24;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -74,6 +79,10 @@ int check_tokens(const hypic_layout *L, const hypic_tokens *x, bool need_q) {
     }
     if (needs_beta(L->family) && (x->b_tok_stride < 0 || x->b_chain_stride < 0))
         return fail(HYPIC_E_INVALID, "negative beta stride");
+    // token offsets inside a chunk or seam window are 32-bit in the kernels
+    if (x->tok_stride > kMaxTokStride || (needs_g(L->family) && x->g_tok_stride > kMaxTokStride) ||
+        (needs_beta(L->family) && x->b_tok_stride > kMaxTokStride))
+        return fail(HYPIC_E_UNSUPPORTED, "token strides above 2^24 elements are not supported");
     return HYPIC_OK;
 }
 
@@ -100,6 +109,81 @@ int launched(hipError_t e, const char *what) {
 }
 
 bool dense(int f) { return f == HYPIC_DELTANET || f == HYPIC_GDN || f == HYPIC_KDA; }
+
+// HYPIC_VALIDATE=1: device-resident offsets and slot ids are read back (a
+// synchronous copy on the caller's stream) and checked before any launch.
+bool validate_on() {
+    const char *e = getenv("HYPIC_VALIDATE");
+    return e && e[0] == '1';
+}
+
+// HYPIC_FAULT_INJECT: "1" or "all" fails every call that would launch, one of
+// "build", "compose", "seam" only that call, with HYPIC_E_DEVICE after its
+// arguments have been validated; nothing is enqueued.  A host-side stand-in
+// for a failed launch, so that callers can test their error paths without
+// making the GPU fail.
+int injected(const char *op) {
+    const char *e = getenv("HYPIC_FAULT_INJECT");
+    if (!e || !e[0] || !strcmp(e, "0")) return HYPIC_OK;
+    if (!strcmp(e, "1") || !strcmp(e, "all") || !strcmp(e, op))
+        return fail(HYPIC_E_DEVICE, "%s launch: fault injected (HYPIC_FAULT_INJECT=%s)", op, e);
+    return HYPIC_OK;
+}
+
+template <typename T>
+int read_back(std::vector<T> &h, const T *d, size_t n, hipStream_t st, const char *what) {
+    h.resize(n);
+    if (n == 0) return HYPIC_OK;
+    hipError_t e = hipMemcpyAsync(h.data(), d, n * sizeof(T), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(HYPIC_E_DEVICE, "HYPIC_VALIDATE: reading %s: %s", what, hipGetErrorString(e));
+    return HYPIC_OK;
+}
+
+int validate_segments(int n_seg, const int64_t *d_b, const int64_t *d_e, int64_t max_len, hipStream_t st) {
+    std::vector<int64_t> b, e;
+    int rc = read_back(b, d_b, n_seg, st, "d_seg_begin");
+    if (!rc) rc = read_back(e, d_e, n_seg, st, "d_seg_end");
+    if (rc) return rc;
+    for (int s = 0; s < n_seg; ++s) {
+        if (b[s] < 0 || e[s] < b[s])
+            return fail(HYPIC_E_INVALID, "HYPIC_VALIDATE: segment %d has range [%lld, %lld)", s, (long long)b[s],
+                        (long long)e[s]);
+        if (e[s] - b[s] > max_len)
+            return fail(HYPIC_E_INVALID, "HYPIC_VALIDATE: segment %d is %lld tokens, above max_seg_len %lld", s,
+                        (long long)(e[s] - b[s]), (long long)max_len);
+    }
+    return HYPIC_OK;
+}
+
+int validate_lists(int n_req, int max_list, const int32_t *d_off, const int32_t *d_pid, int64_t n_slots,
+                   const int64_t *d_sb, hipStream_t st) {
+    std::vector<int32_t> off, pid;
+    std::vector<int64_t> sb;
+    int rc = read_back(off, d_off, (size_t)n_req + 1, st, "d_list_off");
+    if (rc) return rc;
+    if (off[0] < 0) return fail(HYPIC_E_INVALID, "HYPIC_VALIDATE: d_list_off[0] = %d < 0", off[0]);
+    for (int r = 0; r < n_req; ++r) {
+        const int len = off[r + 1] - off[r];
+        if (len < 0 || len > max_list)
+            return fail(HYPIC_E_INVALID, "HYPIC_VALIDATE: request %d has %d entries (max_list_len %d)", r, len, max_list);
+    }
+    const int e0 = off[0], n = off[n_req] - off[0];
+    if (n == 0) return HYPIC_OK;
+    if (!d_pid) return fail(HYPIC_E_INVALID, "HYPIC_VALIDATE: entries but no d_pair_id");
+    if ((rc = read_back(pid, d_pid + e0, n, st, "d_pair_id"))) return rc;
+    for (int i = 0; i < n; ++i)
+        if (pid[i] < 0 || pid[i] >= n_slots)
+            return fail(HYPIC_E_INVALID, "HYPIC_VALIDATE: entry %d names slot %d (n_slots %lld)", e0 + i, pid[i],
+                        (long long)n_slots);
+    if (d_sb) {
+        if ((rc = read_back(sb, d_sb + e0, n, st, "d_seam_begin"))) return rc;
+        for (int i = 0; i < n; ++i)
+            if (sb[i] < -1)
+                return fail(HYPIC_E_INVALID, "HYPIC_VALIDATE: entry %d has seam start %lld", e0 + i, (long long)sb[i]);
+    }
+    return HYPIC_OK;
+}
 
 }  // namespace
 
@@ -151,7 +235,7 @@ int tree_block(int max_list, int64_t chains) {
 
 struct TreeLayout {
     int B, NB;
-    size_t off_aggT, off_aggS, off_sin, off_pvec, total;
+    size_t off_aggT, off_aggS, off_sin, off_pvec, off_blk, total;
 };
 
 TreeLayout tree_layout(const hypic_layout *L, int n_req, int max_list, int w) {
@@ -165,7 +249,8 @@ TreeLayout tree_layout(const hypic_layout *L, int n_req, int max_list, int w) {
     t.off_aggS = al(agg);
     t.off_sin = t.off_aggS + al(agg);
     t.off_pvec = t.off_sin + al(agg);
-    t.total = t.off_pvec + al(pv);
+    t.off_blk = t.off_pvec + al(pv);
+    t.total = t.off_blk + al(((size_t)n_req * t.NB + 1) * sizeof(int32_t));
     return t;
 }
 
@@ -195,7 +280,9 @@ int hypic_segment_build(const hypic_layout *L, const hypic_tokens *x, int32_t n_
     if (L->family == HYPIC_KDA &&
         (!aligned16(x->g) || ((x->g_tok_stride * esize(L->in_dtype)) & 15) || ((x->g_chain_stride * esize(L->in_dtype)) & 15)))
         return fail(HYPIC_E_INVALID, "KDA log-gate rows must be 16-byte aligned");
-    if (x->tok_stride > (1 << 24)) return fail(HYPIC_E_UNSUPPORTED, "tok_stride above 2^24 elements is not supported");
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (validate_on() && (rc = validate_segments(n_seg, d_seg_begin, d_seg_end, max_seg_len, st))) return rc;
+    if ((rc = injected("build"))) return rc;
     hy::BuildArgs a;
     a.x = to_tok(x);
     a.n_chains = L->n_chains;
@@ -206,7 +293,6 @@ int hypic_segment_build(const hypic_layout *L, const hypic_tokens *x, int32_t n_
     a.S = d_S;
     const int D = padded_d(L->dk);
     const bool bf = L->in_dtype == HYPIC_BF16;
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (L->family == HYPIC_KDA) return launched(hy::build_kda(a, bf, D, n_seg, st), "KDA build launch");
     if (dense(L->family)) {
         if (bf) return launched(hy::build_dense_pipe(a, L->family, D, n_seg, st), "dense build launch");
@@ -218,7 +304,7 @@ int hypic_segment_build(const hypic_layout *L, const hypic_tokens *x, int32_t n_
 int hypic_compose(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t max_list_len, const int32_t *d_list_off,
                   const int32_t *d_pair_id, int64_t n_slots, const float *d_T, const float *d_S,
                   const hypic_tokens *seam, const int64_t *d_seam_begin, int32_t w, float *d_state, float *d_o,
-                  void *d_ws, size_t ws_bytes, void *stream) {
+                  float *d_prefix_states, void *d_ws, size_t ws_bytes, void *stream) {
     int rc = check_layout(L);
     if (rc) return rc;
     if (mode != HYPIC_SEQ && mode != HYPIC_TREE) return fail(HYPIC_E_INVALID, "unknown mode %d", mode);
@@ -247,12 +333,20 @@ int hypic_compose(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t ma
     a.seam_begin = d_seam_begin;
     a.state = d_state;
     a.o = d_o;
+    a.prefix = d_prefix_states;
     const bool bf = L->in_dtype == HYPIC_BF16;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    TreeLayout tl{};
+    if (mode == HYPIC_TREE) {
+        tl = tree_layout(L, n_req, max_list_len, has_seam ? w : 0);
+        if (!d_ws || ws_bytes < tl.total)
+            return fail(HYPIC_E_WORKSPACE, "tree compose needs %zu workspace bytes (got %zu)", tl.total, ws_bytes);
+    }
+    if (validate_on() &&
+        (rc = validate_lists(n_req, max_list_len, d_list_off, d_pair_id, n_slots, has_seam ? d_seam_begin : nullptr, st)))
+        return rc;
+    if ((rc = injected("compose"))) return rc;
     if (mode == HYPIC_SEQ) return launched(hy::compose_seq(a, L->family, bf, padded_d(L->dk), n_req, st), "compose launch");
-    const TreeLayout tl = tree_layout(L, n_req, max_list_len, has_seam ? w : 0);
-    if (!d_ws || ws_bytes < tl.total)
-        return fail(HYPIC_E_WORKSPACE, "tree compose needs %zu workspace bytes (got %zu)", tl.total, ws_bytes);
     if (max_list_len == 0) return ok();
     hy::TreeArgs t;
     t.c = a;
@@ -264,6 +358,7 @@ int hypic_compose(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t ma
     t.aggS = reinterpret_cast<float *>(base + tl.off_aggS);
     t.sin = reinterpret_cast<float *>(base + tl.off_sin);
     t.pvec = reinterpret_cast<float *>(base + tl.off_pvec);
+    t.blk_off = reinterpret_cast<int32_t *>(base + tl.off_blk);
     return launched(hy::compose_tree(t, L->family, bf, padded_d(L->dk), n_req, st), "tree compose launch");
 }
 
@@ -277,6 +372,14 @@ int hypic_seam_advance(const hypic_layout *L, const hypic_tokens *x, int32_t n_i
     if (n_items == 0 || w == 0) return ok();
     if (!d_tok_begin || !d_state || !d_o) return fail(HYPIC_E_INVALID, "NULL pointer");
     if ((int64_t)n_items * L->n_chains > 0x7fffffff) return fail(HYPIC_E_INVALID, "n_items * n_chains too large");
+    if (validate_on()) {
+        std::vector<int64_t> tb;
+        if ((rc = read_back(tb, d_tok_begin, n_items, reinterpret_cast<hipStream_t>(stream), "d_tok_begin"))) return rc;
+        for (int i = 0; i < n_items; ++i)
+            if (tb[i] < 0)
+                return fail(HYPIC_E_INVALID, "HYPIC_VALIDATE: item %d starts at token %lld", i, (long long)tb[i]);
+    }
+    if ((rc = injected("seam"))) return rc;
     hy::SeamArgs a;
     a.x = to_tok(x);
     a.n_chains = L->n_chains;

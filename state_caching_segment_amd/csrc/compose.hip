@@ -89,6 +89,7 @@ k_compose_seq(ComposeArgs a) {
             apply_dense_T<D, F32>(X, Tp, dk, Sp, c0);
         else
             apply_diag_T_buf<D>(X, Tp, a.t_elems, dk, Sp, c0);
+        if (a.prefix) store_tile_buf<D>(X, a.prefix + ((int64_t)e * a.n_chains + chain) * dk * dk, dk, c0);
     }
     if constexpr (fam_dense(FAM))
         store_tile<D>(X, st, dk, dk, c0, dk);
@@ -428,6 +429,7 @@ k_compose_dense(TreeArgs t) {
                     for (int nt = 0; nt < 2; ++nt) X[rt][nt] += quad_transpose(spre[rt][nt], lane);
             }
         }
+        if (!TREE && a.prefix) store_tile_buf<D>(X, a.prefix + ((int64_t)e * a.n_chains + chain) * dk * dk, dk, c0);
         if (j + 1 < m) t_put((j + 1) & 1);  // that buffer's last readers finished entry j - 1
         t_load(j + 2 < m ? j + 2 : m - 1);
         __syncthreads();
@@ -467,7 +469,9 @@ k_compose_dense(TreeArgs t) {
 // are the request's block aggregates (slot req * NB + b of aggT / aggS, no
 // seams), and the state entering each block is stored to sin before its
 // product.
-template <int D, int FAM, bool SCAN = false>
+// PREFIX: also store the state after every entry to a.prefix (a separate
+// instantiation, so that the plain form carries no trace of it).
+template <int D, int FAM, bool SCAN = false, bool PREFIX = false>
 __global__ void __launch_bounds__(D / 32 * 64, 2)
 k_compose_lean(TreeArgs targ) {
     static_assert(D >= 64 && (FAM == DELTANET || FAM == GDN), "lean compose: d >= 64, scalar-gate erasing families");
@@ -650,6 +654,21 @@ k_compose_lean(TreeArgs targ) {
             for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) X[rt][nt][jj] += spre[rt][nt][jj];
+        if constexpr (PREFIX && !SCAN) {
+            // the state after entry e
+            const auto r = buffer_view(a.prefix + ((int64_t)e * a.n_chains + chain) * dk * dk, D * D * 4);
+            const int voff = ((int)((unsigned)ln >> 4) * 4 * D + c0 + (int)((unsigned)ln & 15)) * 4;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const float v = X[rt][nt][jj];
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff,
+                                                              ((16 * rt + jj) * D + 16 * nt) * 4, 0);
+                    }
+        }
         // (every product is issued before the barrier, so that the B operands
         // are dead in the staging phase)
         __builtin_amdgcn_sched_barrier(0);
@@ -944,6 +963,21 @@ k_tree_fix_mma(TreeArgs t) {
     }
 }
 
+// Entry offsets of every (request, block) as its own list: block b of request
+// r holds entries list_off[r] + b B .. list_off[r] + min((b + 1) B, len) - 1,
+// so consecutive blocks share their bounds and blocks past a request's end
+// are empty.  A sequential compose over these lists, started from the states
+// entering each block, re-walks the blocks in parallel.
+__global__ void k_block_offsets(const int32_t *list_off, int n_req, int B, int NB, int32_t *blk_off) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n_req * NB) {
+        const int r = i / NB, b = i % NB;
+        const int len = list_off[r + 1] - list_off[r];
+        blk_off[i] = list_off[r] + (b * B < len ? b * B : len);
+    }
+    if (i == 0) blk_off[n_req * NB] = list_off[n_req];
+}
+
 // ---- launchers ----------------------------------------------------------------
 
 #define HY_DISPATCH_FAMILY(FN, ARGS, D, TIN)          \
@@ -964,7 +998,10 @@ static hipError_t launch_compose(const ComposeArgs &a, int n_req, hipStream_t st
     if constexpr (std::is_same<TIN, bf16>::value && D >= 64 && (FAM == DELTANET || FAM == GDN)) {
         TreeArgs t{};
         t.c = a;
-        hipLaunchKernelGGL((k_compose_lean<D, FAM, false>), grid, block, 0, st, t);
+        if (a.prefix)
+            hipLaunchKernelGGL((k_compose_lean<D, FAM, false, true>), grid, block, 0, st, t);
+        else
+            hipLaunchKernelGGL((k_compose_lean<D, FAM, false, false>), grid, block, 0, st, t);
     } else if constexpr (fam_dense(FAM)) {
         TreeArgs t{};
         t.c = a;
@@ -1005,6 +1042,19 @@ static hipError_t launch_tree(const TreeArgs &t, int n_req, hipStream_t st) {
                            dim3(D / 32 * 64), 0, st, t);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (t.c.prefix) {
+        // The states after every entry: each block is re-walked from the state
+        // entering it by the sequential compose, which also writes its seam
+        // outputs whole (so the fix-up is not needed).
+        const int nblk = n_req * t.NB;
+        hipLaunchKernelGGL(k_block_offsets, dim3((unsigned)((nblk + 256) / 256)), dim3(256), 0, st, t.c.list_off, n_req,
+                           t.B, t.NB, t.blk_off);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        ComposeArgs rw = t.c;
+        rw.list_off = t.blk_off;
+        rw.state = t.sin;
+        return launch_compose<D, FAM, TIN>(rw, nblk, st);
+    }
     if (t.c.has_seam) {
         if constexpr (std::is_same<TIN, bf16>::value && D >= 64)
             hipLaunchKernelGGL((k_tree_fix_mma<D>), dim3(blocks), dim3(D / 32 * 64), 0, st, t);

@@ -29,8 +29,9 @@ struct ComposeArgs {
     const float *S;
     int64_t t_elems;
     const int64_t *seam_begin;
-    float *state;  // [req][chain][dk][dk]
-    float *o;      // [entry][w][chain][dk]
+    float *state;   // [req][chain][dk][dk]
+    float *o;       // [entry][w][chain][dk]
+    float *prefix;  // [entry][chain][dk][dk]: state after each entry, or null
 };
 
 struct SeamArgs {
@@ -52,6 +53,7 @@ struct TreeArgs {
     float *aggS;
     float *sin;    // [req][NB][chain][dk][dk] state entering each block
     float *pvec;   // [req][max_list][w][chain][dk] pulled-back seam queries
+    int32_t *blk_off;  // [req * NB + 1] entry offsets of every block (prefix states only)
 };
 
 // D is the padded state size (32, 64 or 128) the kernel is instantiated for.

@@ -65,7 +65,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hypic_workspace_bytes.restype = sz
     lib.hypic_segment_build.argtypes = [P, P, i32, P, P, i64, P, P, P, sz, P]
     lib.hypic_segment_build.restype = ctypes.c_int
-    lib.hypic_compose.argtypes = [P, i32, i32, i32, P, P, i64, P, P, P, P, i32, P, P, P, sz, P]
+    lib.hypic_compose.argtypes = [P, i32, i32, i32, P, P, i64, P, P, P, P, i32, P, P, P, P, sz, P]
     lib.hypic_compose.restype = ctypes.c_int
     lib.hypic_seam_advance.argtypes = [P, P, i32, P, i32, P, P, P]
     lib.hypic_seam_advance.restype = ctypes.c_int
@@ -132,11 +132,11 @@ def hypic_segment_build(L: hypic_layout, x: hypic_tokens, n_seg: int, seg_begin,
 
 
 def hypic_compose(L: hypic_layout, mode: int, n_req: int, max_list_len: int, list_off, pair_id, n_slots: int,
-                  T, S, seam: Optional[hypic_tokens], seam_begin, w: int, state, o, ws=None, ws_bytes: int = 0,
-                  stream=None) -> None:
+                  T, S, seam: Optional[hypic_tokens], seam_begin, w: int, state, o, prefix_states=None, ws=None,
+                  ws_bytes: int = 0, stream=None) -> None:
     _check(load().hypic_compose(ctypes.byref(L), mode, n_req, max_list_len, _p(list_off), _p(pair_id), n_slots,
                                 _p(T), _p(S), ctypes.byref(seam) if seam is not None else None, _p(seam_begin), w,
-                                _p(state), _p(o), _p(ws), ws_bytes, _stream(stream)))
+                                _p(state), _p(o), _p(prefix_states), _p(ws), ws_bytes, _stream(stream)))
 
 
 def hypic_seam_advance(L: hypic_layout, x: hypic_tokens, n_items: int, tok_begin, w: int, state, o,

@@ -20,9 +20,10 @@ FLOOR = 2.0 ** -100
 TOL = {"f32": 1e-4, "bf16": 5e-3}
 
 
-def gpu_request(wl, w=None, stream=None, mode=None, slot_order="request"):
+def gpu_request(wl, w=None, stream=None, mode=None, slot_order="request", prefix=False):
     """Build every segment body's pair, then compose each request with its seams
-    (sequential compose, or the tree scan with mode=hy.TREE)."""
+    (sequential compose, or the tree scan with mode=hy.TREE); with prefix=True
+    the state after every entry is returned too."""
     mode = hy.SEQ if mode is None else mode
     w = wl.w if w is None else w
     plan = request_plan(wl.requests, w, slot_order=slot_order)
@@ -44,10 +45,12 @@ def gpu_request(wl, w=None, stream=None, mode=None, slot_order="request"):
     if mode == hy.TREE:
         nws = hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, plan.n_req, plan.max_list_len, w)
         ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    pre = (torch.full((len(plan.pair_id), wl.n_chains, wl.dk, wl.dv), float("nan"), device=dev) if prefix
+           else None)
     hy.hypic_compose(L, mode, plan.n_req, plan.max_list_len, lo, pid, plan.n_slots, T, S,
-                     x if w > 0 else None, seam, w, state, o, ws, nws, stream=stream)
+                     x if w > 0 else None, seam, w, state, o, pre, ws, nws, stream=stream)
     torch.cuda.synchronize()
-    return {"plan": plan, "T": T, "S": S, "state": state, "O": o}
+    return {"plan": plan, "T": T, "S": S, "state": state, "O": o, "prefix": pre}
 
 
 def chain_inputs(wl, chains, t0, t1):
@@ -61,16 +64,25 @@ def chain_inputs(wl, chains, t0, t1):
     return cm(wl.q), cm(wl.k), cm(wl.v), cm(wl.g), cm(wl.beta), gam
 
 
-def oracle_request(wl, chains, w=None, nthreads=0, reqs=None):
+def oracle_request(wl, chains, w=None, nthreads=0, reqs=None, parallel=1):
     """The oracle's reuse path for every request (or the requests listed in
-    reqs), on the given chains."""
+    reqs), on the given chains; `parallel` requests at a time (the oracle's
+    calls release the interpreter lock)."""
     w = wl.w if w is None else w
-    out = []
-    for r in (range(len(wl.requests)) if reqs is None else reqs):
+    rs = list(range(len(wl.requests)) if reqs is None else reqs)
+    inputs = []
+    for r in rs:
         b = wl.requests[r]
-        q, k, v, g, beta, gam = chain_inputs(wl, chains, int(b[0]), int(b[-1]))
-        out.append(oracle.request_batch(wl.family, b - b[0], w, q, k, v, g, beta, gam, nthreads=nthreads))
-    return out
+        inputs.append((b, chain_inputs(wl, chains, int(b[0]), int(b[-1]))))
+
+    def one(item):
+        b, (q, k, v, g, beta, gam) = item
+        return oracle.request_batch(wl.family, b - b[0], w, q, k, v, g, beta, gam, nthreads=nthreads)
+    if parallel <= 1:
+        return [one(it) for it in inputs]
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=parallel) as ex:
+        return list(ex.map(one, inputs))
 
 
 def dense_T(Tc: np.ndarray, dk: int) -> np.ndarray:

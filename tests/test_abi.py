@@ -106,16 +106,70 @@ def test_compose_and_seam_validation():
     s(L, x, 0, None, 8, None, None)
 
 
+def test_token_stride_bound():
+    """Token strides above 2^24 elements are refused by every call that reads
+    tokens: offsets inside a chunk or seam window are 32-bit in the kernels."""
+    L = hy.layout("gdn", "f32", 4, 64)
+    big = (1 << 24) + 64
+    expect(-2, hy.hypic_segment_build, L, _fake_tokens("gdn", "f32", ts=big, cs=64), 1, 8, 8, 10, 8, 8)
+    expect(-2, hy.hypic_compose, L, hy.SEQ, 1, 2, 8, 8, 2, 8, 8, _fake_tokens("gdn", "f32", ts=big, cs=64), 8, 8, 8, 8)
+    expect(-2, hy.hypic_seam_advance, L, _fake_tokens("gdn", "f32", ts=big, cs=64), 2, 8, 8, 8, 8)
+    xg = _fake_tokens("gdn", "f32", cs=64)
+    xg.g_tok_stride = big
+    expect(-2, hy.hypic_compose, L, hy.SEQ, 1, 2, 8, 8, 2, 8, 8, xg, 8, 8, 8, 8)
+    xb = _fake_tokens("gdn", "f32", cs=64)
+    xb.b_tok_stride = big
+    expect(-2, hy.hypic_seam_advance, L, xb, 2, 8, 8, 8, 8)
+    # at the bound the checks pass: the fault-injection switch stops the call before any launch
+    ok = _fake_tokens("gdn", "f32", ts=1 << 24, cs=64)
+    os.environ["HYPIC_FAULT_INJECT"] = "all"
+    try:
+        expect(-4, hy.hypic_compose, L, hy.SEQ, 1, 2, 8, 8, 2, 8, 8, ok, 8, 8, 8, 8)
+    finally:
+        del os.environ["HYPIC_FAULT_INJECT"]
+
+
+def test_fault_injection():
+    """HYPIC_FAULT_INJECT fails a valid call with HYPIC_E_DEVICE after its
+    arguments are checked and before anything is enqueued; bad arguments still
+    report their own status first."""
+    L = hy.layout("gdn", "bf16", 4, 64)
+    x = _fake_tokens("gdn", cs=64)
+    try:
+        for val in ("1", "all", "build"):
+            os.environ["HYPIC_FAULT_INJECT"] = val
+            expect(-4, hy.hypic_segment_build, L, x, 1, 8, 8, 10, 8, 8)
+            assert "fault injected" in hy.hypic_last_error()
+            expect(-1, hy.hypic_segment_build, L, x, -1, 8, 8, 10, 8, 8)   # validation first
+        for val in ("1", "compose"):
+            os.environ["HYPIC_FAULT_INJECT"] = val
+            expect(-4, hy.hypic_compose, L, hy.SEQ, 1, 2, 8, 8, 2, 8, 8, x, 8, 8, 8, 8)
+            # tree mode: the workspace check comes before the injected fault
+            expect(-3, hy.hypic_compose, L, hy.TREE, 1, 2, 8, 8, 2, 8, 8, None, None, 0, 8, None)
+            expect(-4, hy.hypic_compose, L, hy.TREE, 1, 2, 8, 8, 2, 8, 8, None, None, 0, 8, None, None, 8,
+                   1 << 30)
+        for val in ("1", "seam"):
+            os.environ["HYPIC_FAULT_INJECT"] = val
+            expect(-4, hy.hypic_seam_advance, L, x, 2, 8, 8, 8, 8)
+        os.environ["HYPIC_FAULT_INJECT"] = "seam"   # other calls unaffected: they reach their own checks
+        expect(-1, hy.hypic_compose, L, hy.SEQ, 1, 2, 8, 8, 2, 8, 8, x, 8, -1, 8, 8)
+        os.environ["HYPIC_FAULT_INJECT"] = "0"
+        expect(-1, hy.hypic_seam_advance, L, x, 2, 8, -3, 8, 8)
+    finally:
+        os.environ.pop("HYPIC_FAULT_INJECT", None)
+
+
 def test_workspace_query():
     L = hy.layout("gdn", "bf16", 4, 128)
     assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_SEQ, 4, 48, 8) == 0
     assert hy.hypic_workspace_bytes(L, hy.OP_BUILD, 4, 48, 8) == 0
     # tree: 3 block-aggregate arrays of n_req x NB x chains x dk^2 fp32, plus seam queries; 16 chains
     # cannot fill the GPU, so blocks of ceil(sqrt(48 / 2)) = 5 entries, NB = 10
+    # (the last term: the block entry offsets, n_req x NB + 1 int32, in whole 256-byte units)
     nb, agg = 10, 4 * 10 * 4 * 128 * 128 * 4
     pv = 4 * 48 * 8 * 4 * 128 * 4
-    assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 4, 48, 8) == 3 * agg + pv
-    assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 4, 48, 0) == 3 * agg
+    assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 4, 48, 8) == 3 * agg + pv + 256
+    assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 4, 48, 0) == 3 * agg + 256
     assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 4, 48, -1) == 0
     assert hy.hypic_workspace_bytes(hy.layout("gdn", "bf16", 4, 100), hy.OP_COMPOSE_TREE, 4, 48, 8) == 0
     # 16 requests x 32 chains (one KDA layer) of 128 entries: the chains fill the GPU, so 4 blocks
@@ -123,14 +177,14 @@ def test_workspace_query():
     L = hy.layout("kda", "bf16", 32, 128)
     agg = 16 * 4 * 32 * 128 * 128 * 4
     pv = 16 * 128 * 8 * 32 * 128 * 4
-    assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 16, 128, 8) == 3 * agg + pv
+    assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 16, 128, 8) == 3 * agg + pv + 512
     # one request of 32 entries on 16 GLA chains: 16 x 6 blocks cannot fill the GPU, so blocks of
     # ceil(sqrt(32 / 2)) = 4 entries, NB = 8 (GLA's aggregates are still dk x dk fp32 states)
     L = hy.layout("gla", "bf16", 16, 128)
-    assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 1, 32, 0) == 3 * (1 * 8 * 16 * 128 * 128 * 4)
+    assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 1, 32, 0) == 3 * (1 * 8 * 16 * 128 * 128 * 4) + 256
     # 5000 entries on 512 chains: longer blocks are capped at 64 entries, NB = ceil(5000 / 64) = 79
     L = hy.layout("gdn", "bf16", 32, 64)
-    assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 16, 5000, 0) == 3 * (16 * 79 * 32 * 64 * 64 * 4)
+    assert hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 16, 5000, 0) == 3 * (16 * 79 * 32 * 64 * 64 * 4) + 5120
 
 
 def test_request_plan():

@@ -60,6 +60,7 @@ def test_kda(dtype, d):
 
 @pytest.mark.parametrize("fam,dtype,d", [("gdn", "bf16", 128), ("kda", "bf16", 128), ("gla", "bf16", 64),
                                          ("gla", "bf16", 128), ("retnet", "f32", 32), ("retnet", "bf16", 16),
+                                         ("retnet", "f32", 64),
                                          ("deltanet", "f32", 16), ("mamba2", "bf16", 64), ("linear", "f32", 64),
                                          ("deltanet", "bf16", 128), ("kda", "bf16", 64), ("kda", "bf16", 16),
                                          ("gdn", "bf16", 32)])
@@ -101,6 +102,8 @@ def test_retnet_c2_closed_form_and_naive_addition():
     linear layers)."""
     wl = workloads.config("c2", device="cuda")
     gpu, _ = check(wl)
+    # (8 chains x 8 entries: the tree with blocks of 2 entries, as bench.py composes it)
+    check(wl, mode=hy.TREE, label="c2_tree")
     plan = gpu["plan"]
     lens = plan.seg_end - plan.seg_begin
     gam = wl.gamma.double().cpu().numpy()
@@ -286,18 +289,71 @@ def test_gdn_full_request_sampled():
     assert_close(err, TOL["bf16"], "c4")
 
 
+@pytest.mark.parametrize("name", ["c4_deltanet", "c4_slowgdn"])
+def test_c4_stressors_full_request_sampled(name):
+    """The full 960-chain, 32768-token request with gates under which T
+    carries real weight: DeltaNet (no decay) and slow-gate GDN (gates
+    -softplus(N(-7, 0.5)), T of a 680-token segment about 0.5 in norm).  At
+    the headline gate law the long segments' T fall under 2^-100; here every
+    T is checked against the oracle, on a seeded 16-chain sample with the
+    first and last chain."""
+    wl = workloads.config(name, device="cuda")
+    rng = np.random.default_rng(405)
+    chains = sorted(set([0, 959]) | set(rng.choice(np.arange(1, 959), 14, replace=False).tolist()))
+    assert len(chains) == 16
+    gpu = gpu_request(wl)
+    for key in ("T", "S", "state", "O"):
+        assert torch.isfinite(gpu[key]).all(), key
+    ref = oracle_request(wl, chains)
+    err = compare(wl, gpu, ref, chains)
+    print(name, "sampled", err, flush=True)
+    assert err["T_floor"] == 0, "the stressors are meant to keep every T above the floor"
+    assert_close(err, TOL["bf16"], name)
+
+
 def test_kda_c5_full_layer_sampled():
     """KDA, one layer at full size: 32 heads, 16 requests of 100000 tokens in
     128 lognormal segments each, w = 8; every segment built and every request
     composed by the tree scan on the GPU (the kernels the KDA bench line
-    times); the oracle's full path for the first and last request on the
-    first and last head."""
+    times); the oracle's full path on 16 (request, head) chains: requests 0,
+    5, 10 and 15 on heads 0, 10, 21 and 31 (first and last of each)."""
     wl = workloads.config("c5", device="cuda")
     gpu = gpu_request(wl, mode=hy.TREE)
     for key in ("T", "S", "state", "O"):
         assert torch.isfinite(gpu[key]).all(), key
-    chains, reqs = [0, wl.n_chains - 1], [0, len(wl.requests) - 1]
-    ref = oracle_request(wl, chains, nthreads=len(chains), reqs=reqs)
+    chains, reqs = [0, 10, 21, wl.n_chains - 1], [0, 5, 10, len(wl.requests) - 1]
+    ref = oracle_request(wl, chains, nthreads=len(chains), reqs=reqs, parallel=len(reqs))
     err = compare(wl, gpu, ref, chains, reqs=reqs)
     print("c5 sampled", err, flush=True)
     assert_close(err, TOL["bf16"], "c5")
+
+
+@pytest.mark.parametrize("fam,d", [("gdn", 128), ("kda", 128)])
+def test_long_list_sequential(fam, d):
+    """A request of 160 segments (short bodies): the sequential compose
+    reloads its 64-entry window of pair ids and seam starts twice."""
+    rng = np.random.default_rng(160)
+    lens = (rng.integers(9, 30, 160)).tolist()
+    laws = workloads.KDA_LAWS if fam == "kda" else workloads.GDN_LAWS
+    wl = workloads.make(f"long_{fam}", config_id=46, family=fam, dtype="bf16", n_chains=2, d=d, lens=lens, w=8,
+                        laws=laws, device="cuda")
+    check(wl, label=f"long_{fam}_seq")
+
+
+@pytest.mark.parametrize("fam,d,m", [("gdn", 64, 8000), ("kda", 64, 7900)])
+def test_long_list_tree_few_chains(fam, d, m):
+    """One chain, thousands of entries: the tree takes blocks of 64 (m =
+    8000) or 63 (m = 7900) entries, so each block reloads its entry window, and
+    125 or 126 block aggregates, so the scan over them reloads its window
+    too."""
+    rng = np.random.default_rng(m)
+    lens = rng.integers(9, 13, m).tolist()
+    laws = workloads.KDA_LAWS if fam == "kda" else workloads.GDN_LAWS
+    wl = workloads.make(f"tree_long_{fam}", config_id=47, family=fam, dtype="bf16", n_chains=1, d=d, lens=lens,
+                        w=8, laws=laws, device="cuda")
+    L = hy.layout(fam, "bf16", 1, d)
+    nws = hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 1, m, 8)
+    nb = 125 if m == 8000 else 126
+    agg = nb * d * d * 4
+    assert nws == 3 * agg + m * 8 * d * 4 + 512, "blocking of this case changed"
+    check(wl, mode=hy.TREE, label=f"tree_long_{fam}_{m}")
