@@ -191,6 +191,27 @@ int hypic_compose(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t ma
                   float *d_prefix_states, void *d_ws, size_t ws_bytes, void *stream);
 
 /*
+ * hypic_compose_tree_noalloc -- hypic_compose in HYPIC_TREE mode for callers
+ * that cannot allocate device memory (code under graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Arguments and results are those
+ * of hypic_compose with mode HYPIC_TREE; the workspace is the library's own:
+ * HYPIC_NOALLOC_WORKSPACE_BYTES of device memory per GPU, part of the loaded
+ * code object and held until the process ends.  The call allocates nothing.
+ * A call whose workspace (hypic_workspace_bytes with HYPIC_OP_COMPOSE_TREE)
+ * would exceed it returns HYPIC_E_WORKSPACE before any HIP call.  Every call
+ * on one GPU shares that GPU's workspace: calls that overlap on one GPU (on
+ * different streams, or from different threads) race and give undefined
+ * results; calls on one stream are ordered and safe.  Nothing in the
+ * workspace needs to start at any value.
+ */
+#define HYPIC_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+int hypic_compose_tree_noalloc(const hypic_layout *L, int32_t n_req, int32_t max_list_len,
+                               const int32_t *d_list_off, const int32_t *d_pair_id, int64_t n_slots,
+                               const float *d_T, const float *d_S, const hypic_tokens *seam,
+                               const int64_t *d_seam_begin, int32_t w, float *d_state, float *d_o,
+                               float *d_prefix_states, void *stream);
+
+/*
  * hypic_seam_advance -- advance n_items independent states through w tokens
  * each (codernav.top, seam windows: the linear layers compute the window's
  * transition and state on the fly, advance the running state and emit each

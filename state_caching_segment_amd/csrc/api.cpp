@@ -301,10 +301,16 @@ int hypic_segment_build(const hypic_layout *L, const hypic_tokens *x, int32_t n_
     return launched(hy::build_diag(a, L->family, bf, D, n_seg, st), "diagonal build launch");
 }
 
-int hypic_compose(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t max_list_len, const int32_t *d_list_off,
-                  const int32_t *d_pair_id, int64_t n_slots, const float *d_T, const float *d_S,
-                  const hypic_tokens *seam, const int64_t *d_seam_begin, int32_t w, float *d_state, float *d_o,
-                  float *d_prefix_states, void *d_ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// hypic_compose; lib_ws: the tree's workspace is the library's own (d_ws and
+// ws_bytes unused), whose address is taken only once a launch is due.
+int compose_call(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t max_list_len, const int32_t *d_list_off,
+                 const int32_t *d_pair_id, int64_t n_slots, const float *d_T, const float *d_S,
+                 const hypic_tokens *seam, const int64_t *d_seam_begin, int32_t w, float *d_state, float *d_o,
+                 float *d_prefix_states, void *d_ws, size_t ws_bytes, bool lib_ws, void *stream) {
     int rc = check_layout(L);
     if (rc) return rc;
     if (mode != HYPIC_SEQ && mode != HYPIC_TREE) return fail(HYPIC_E_INVALID, "unknown mode %d", mode);
@@ -339,7 +345,12 @@ int hypic_compose(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t ma
     TreeLayout tl{};
     if (mode == HYPIC_TREE) {
         tl = tree_layout(L, n_req, max_list_len, has_seam ? w : 0);
-        if (!d_ws || ws_bytes < tl.total)
+        if (lib_ws && tl.total > hy::kStaticWorkspaceBytes)
+            return fail(HYPIC_E_WORKSPACE,
+                        "tree compose of %d requests x %d chains, %d entries, w=%d needs %zu workspace bytes; the "
+                        "library's own workspace holds %zu (hypic_compose takes a caller workspace)",
+                        n_req, L->n_chains, max_list_len, has_seam ? w : 0, tl.total, hy::kStaticWorkspaceBytes);
+        if (!lib_ws && (!d_ws || ws_bytes < tl.total))
             return fail(HYPIC_E_WORKSPACE, "tree compose needs %zu workspace bytes (got %zu)", tl.total, ws_bytes);
     }
     if (validate_on() &&
@@ -348,6 +359,10 @@ int hypic_compose(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t ma
     if ((rc = injected("compose"))) return rc;
     if (mode == HYPIC_SEQ) return launched(hy::compose_seq(a, L->family, bf, padded_d(L->dk), n_req, st), "compose launch");
     if (max_list_len == 0) return ok();
+    if (lib_ws) {
+        const hipError_t e = hy::static_workspace(&d_ws);
+        if (e != hipSuccess) return fail(HYPIC_E_DEVICE, "library workspace address: %s", hipGetErrorString(e));
+    }
     hy::TreeArgs t;
     t.c = a;
     t.B = tl.B;
@@ -360,6 +375,28 @@ int hypic_compose(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t ma
     t.pvec = reinterpret_cast<float *>(base + tl.off_pvec);
     t.blk_off = reinterpret_cast<int32_t *>(base + tl.off_blk);
     return launched(hy::compose_tree(t, L->family, bf, padded_d(L->dk), n_req, st), "tree compose launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int hypic_compose(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t max_list_len, const int32_t *d_list_off,
+                  const int32_t *d_pair_id, int64_t n_slots, const float *d_T, const float *d_S,
+                  const hypic_tokens *seam, const int64_t *d_seam_begin, int32_t w, float *d_state, float *d_o,
+                  float *d_prefix_states, void *d_ws, size_t ws_bytes, void *stream) {
+    return compose_call(L, mode, n_req, max_list_len, d_list_off, d_pair_id, n_slots, d_T, d_S, seam, d_seam_begin, w,
+                        d_state, d_o, d_prefix_states, d_ws, ws_bytes, false, stream);
+}
+
+static_assert(hy::kStaticWorkspaceBytes == HYPIC_NOALLOC_WORKSPACE_BYTES, "header and library disagree");
+
+int hypic_compose_tree_noalloc(const hypic_layout *L, int32_t n_req, int32_t max_list_len, const int32_t *d_list_off,
+                               const int32_t *d_pair_id, int64_t n_slots, const float *d_T, const float *d_S,
+                               const hypic_tokens *seam, const int64_t *d_seam_begin, int32_t w, float *d_state,
+                               float *d_o, float *d_prefix_states, void *stream) {
+    return compose_call(L, HYPIC_TREE, n_req, max_list_len, d_list_off, d_pair_id, n_slots, d_T, d_S, seam,
+                        d_seam_begin, w, d_state, d_o, d_prefix_states, nullptr, 0, true, stream);
 }
 
 int hypic_seam_advance(const hypic_layout *L, const hypic_tokens *x, int32_t n_items, const int64_t *d_tok_begin,

@@ -29,6 +29,8 @@
 //   3. per (request, block, chain): o_t = o^_t + S_in^T p_t.
 // Every pair is read once; the price is the T T_p product (about twice the
 // sequential flops).
+#include <mutex>
+
 #include "compose_common.h"
 #include "kernels.h"
 
@@ -976,6 +978,32 @@ __global__ void k_block_offsets(const int32_t *list_off, int n_req, int B, int N
         blk_off[i] = list_off[r] + (b * B < len ? b * B : len);
     }
     if (i == 0) blk_off[n_req * NB] = list_off[n_req];
+}
+
+// ---- the library's own tree workspace ------------------------------------------
+// For callers that cannot allocate device memory: a fixed-size workspace in
+// the code object, one copy per GPU, held until the process ends.  Host code
+// never passes the array's name to a kernel (on the host that name is only a
+// stand-in); the device address comes from hipGetSymbolAddress, once per
+// device, and is kept per device.
+static __device__ __align__(256) char scratch[kStaticWorkspaceBytes];
+
+hipError_t static_workspace(void **ptr) {
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 // ---- launchers ----------------------------------------------------------------

@@ -65,4 +65,11 @@ hipError_t compose_seq(const ComposeArgs &a, int family, bool bf16_in, int D, in
 hipError_t compose_tree(const TreeArgs &t, int family, bool bf16_in, int D, int n_req, hipStream_t st);
 hipError_t seam_advance(const SeamArgs &a, int family, bool bf16_in, int D, int n_items, hipStream_t st);
 
+// The library's own tree-compose workspace: kStaticWorkspaceBytes of device
+// memory per GPU (a file-scope device array), its address on the current
+// device in *ptr.  Every call on one GPU shares it.
+constexpr size_t kStaticWorkspaceBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t static_workspace(void **ptr);
+
 }  // namespace hy

@@ -25,7 +25,8 @@ OP_BUILD, OP_COMPOSE_SEQ, OP_COMPOSE_TREE, OP_SEAM = 0, 1, 2, 3
 STATUS = {0: "HYPIC_OK", -1: "HYPIC_E_INVALID", -2: "HYPIC_E_UNSUPPORTED", -3: "HYPIC_E_WORKSPACE",
           -4: "HYPIC_E_DEVICE"}
 EXPORTS = ("hypic_t_elems", "hypic_workspace_bytes", "hypic_segment_build", "hypic_compose",
-           "hypic_seam_advance", "hypic_status_string", "hypic_last_error")
+           "hypic_compose_tree_noalloc", "hypic_seam_advance", "hypic_status_string", "hypic_last_error")
+NOALLOC_WORKSPACE_BYTES = 64 << 20  # HYPIC_NOALLOC_WORKSPACE_BYTES
 
 
 class HypicError(RuntimeError):
@@ -67,6 +68,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hypic_segment_build.restype = ctypes.c_int
     lib.hypic_compose.argtypes = [P, i32, i32, i32, P, P, i64, P, P, P, P, i32, P, P, P, P, sz, P]
     lib.hypic_compose.restype = ctypes.c_int
+    lib.hypic_compose_tree_noalloc.argtypes = [P, i32, i32, P, P, i64, P, P, P, P, i32, P, P, P, P]
+    lib.hypic_compose_tree_noalloc.restype = ctypes.c_int
     lib.hypic_seam_advance.argtypes = [P, P, i32, P, i32, P, P, P]
     lib.hypic_seam_advance.restype = ctypes.c_int
     lib.hypic_status_string.argtypes = [ctypes.c_int]
@@ -137,6 +140,15 @@ def hypic_compose(L: hypic_layout, mode: int, n_req: int, max_list_len: int, lis
     _check(load().hypic_compose(ctypes.byref(L), mode, n_req, max_list_len, _p(list_off), _p(pair_id), n_slots,
                                 _p(T), _p(S), ctypes.byref(seam) if seam is not None else None, _p(seam_begin), w,
                                 _p(state), _p(o), _p(prefix_states), _p(ws), ws_bytes, _stream(stream)))
+
+
+def hypic_compose_tree_noalloc(L: hypic_layout, n_req: int, max_list_len: int, list_off, pair_id, n_slots: int,
+                               T, S, seam: Optional[hypic_tokens], seam_begin, w: int, state, o,
+                               prefix_states=None, stream=None) -> None:
+    _check(load().hypic_compose_tree_noalloc(ctypes.byref(L), n_req, max_list_len, _p(list_off), _p(pair_id),
+                                             n_slots, _p(T), _p(S), ctypes.byref(seam) if seam is not None else None,
+                                             _p(seam_begin), w, _p(state), _p(o), _p(prefix_states),
+                                             _stream(stream)))
 
 
 def hypic_seam_advance(L: hypic_layout, x: hypic_tokens, n_items: int, tok_begin, w: int, state, o,
