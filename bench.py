@@ -13,8 +13,17 @@ segments.  Inputs are seeded synthetic tensors generated on the GPU and
 resident in HBM before timing starts.
 
 Printed: one JSON line with build tokens/s (request tokens / build time) as
-`value`, the compose latency, each kernel's roofline fraction, and the fp64
-oracle timed on the host on a bounded sample of chains.
+`value`, the compose latency, each kernel's roofline fraction, the fused cold
+prefill (outputs of every body token and the pairs in one pass) for the
+dense families, a measured device copy bandwidth beside the vendor peak, and
+the fp64 oracle timed on the host on a bounded sample of chains.
+
+Workloads with cache hits (the KDA layer: 13 cold segments of 128 per
+request) time the build of the cold bodies only and compose with the tree
+scan over the full pair cache; --layers N repeats that for N layers, each on
+fresh inputs generated untimed, and reports the per-layer times and their
+sum.  --ab PATH alternates steps between this library and another build of
+it in the same process (a same-box A/B comparison).
 """
 import argparse
 import json
@@ -101,13 +110,35 @@ def build_kernel(family, dtype):
     return "k_build_diag", ["build_diag.hip", "common.h"]
 
 
-def compose_kernel(family, in_bf16=True, d=128):
-    """The sequential compose kernel the library dispatches for a family, and
-    the sources whose hash keys its stored counter readings."""
+def compose_kernel(family, in_bf16=True, d=128, tree=False):
+    """The compose kernels the library dispatches for a family and mode, and
+    the sources whose hash keys their stored counter readings."""
     files = ["compose.hip", "compose_common.h", "common.h"]
+    dense = family in DENSE
+    if tree:
+        block = "k_compose_dense (tree block)" if dense else "k_tree_block"
+        scan = "k_compose_lean (scan)" if dense and in_bf16 and d >= 64 else "k_tree_scan"
+        fix = "k_tree_fix_mma" if in_bf16 and d >= 64 else "k_tree_fix"
+        return f"{block} + {scan} + {fix}", files
     if family in ("deltanet", "gdn") and in_bf16 and d >= 64:
         return "k_compose_lean", files
-    return ("k_compose_dense" if family in ("deltanet", "gdn", "kda") else "k_compose_seq"), files
+    return ("k_compose_dense" if dense else "k_compose_seq"), files
+
+
+def prefill_cost(family, lens, d, n_chains, in_bytes):
+    """Algorithmic flops and bytes of the fused cold prefill: the pair build
+    plus, per chunk of c tokens, the outputs from the chunk-start state
+    (2 c d^2, none for a segment's first chunk, which starts from zero) and
+    within the chunk (tril(Q K^T): c(c+1) d; times the solved rows: c(c+1) d);
+    bytes add q read and o written (d each, input dtype) per token."""
+    flops, byts = build_cost(family, lens, d, n_chains, in_bytes)
+    extra = 0.0
+    for n in lens:
+        for j, c0 in enumerate(range(0, int(n), CH)):
+            c = min(CH, int(n) - c0)
+            extra += (2 * c * d * d if j > 0 else 0) + 2 * c * (c + 1) * d
+    tokens = float(np.sum(lens))
+    return flops + extra * n_chains, byts + tokens * 2 * d * in_bytes * n_chains
 
 
 def measured_traffic(key, files):
@@ -129,41 +160,199 @@ def measured_traffic(key, files):
     return c["fetch_bytes"] + c["write_bytes"]
 
 
-def cpu_baseline(wl, n_chains_sample, w):
-    """The fp64 oracle (build every pair token by token, compose, seams) on a
-    sample of chains, all host threads; scaled to request tokens/s for all
-    chains."""
+def _chain_major(x, chains, t0=None, t1=None):
+    if x is None:
+        return None
+    y = x if t0 is None else x[t0:t1]
+    return np.ascontiguousarray(np.moveaxis(y[:, chains].double().cpu().numpy(), 1, 0))
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, plan, cold, n_chains_sample, w):
+    """The fp64 oracle timed on the host on a bounded sample of chains, on the
+    work `value` counts, scaled to all chains:
+      - without cache hits: the whole request (every pair built token by
+        token with explicit T, then the compose and the seams);
+      - with cache hits: the pairs of request 0's cold bodies.
+    Threads: all host threads, plus one single-thread time on one chain."""
     import oracle
-    chains = list(range(n_chains_sample))
-    b = wl.requests[0]
-
-    def cm(x):
-        if x is None:
-            return None
-        return np.ascontiguousarray(np.moveaxis(x[:, chains].double().cpu().numpy(), 1, 0))
-
-    q, k, v, g, beta = cm(wl.q), cm(wl.k), cm(wl.v), cm(wl.g), cm(wl.beta)
-    gam = None if wl.gamma is None else wl.gamma[chains].double().cpu().numpy()
     threads = oracle.max_threads()
-    t0 = time.perf_counter()
-    oracle.request_batch(wl.family, b - b[0], w, q, k, v, g, beta, gam, want_pairs=False, nthreads=threads)
-    dt = time.perf_counter() - t0
-    tok = float(b[-1] - b[0])
+
+    def run(chains, nthreads):
+        if cold.all():
+            b = wl.requests[0]
+            q, k, v, g, beta = (_chain_major(t, chains) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+            gam = None if wl.gamma is None else wl.gamma[chains].double().cpu().numpy()
+            t0 = time.perf_counter()
+            oracle.request_batch(wl.family, b - b[0], w, q, k, v, g, beta, gam, want_pairs=False, nthreads=nthreads)
+            return time.perf_counter() - t0, float(b[-1] - b[0])
+        # cold bodies of request 0, one oracle pair per (body, chain), chains on host threads
+        e0, e1 = int(plan.list_off[0]), int(plan.list_off[1])
+        slots = [int(plan.pair_id[e]) for e in range(e0, e1) if cold[int(plan.pair_id[e])]]
+        jobs = []
+        for sl in slots:
+            b, e = int(plan.seg_begin[sl]), int(plan.seg_end[sl])
+            ins = [_chain_major(t, chains, b, e) for t in (wl.k, wl.v, wl.g, wl.beta)]
+            for ci in range(len(chains)):
+                jobs.append([None if t is None else t[ci] for t in ins])
+        from concurrent.futures import ThreadPoolExecutor
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=nthreads) as ex:
+            list(ex.map(lambda j: oracle.pair(wl.family, j[0], j[1], j[2], j[3]), jobs))
+        return time.perf_counter() - t0, float(sum(plan.seg_end[s] - plan.seg_begin[s] for s in slots))
+
+    chains = list(range(n_chains_sample))
+    dt, tok = run(chains, threads)
+    dt1, _ = run([0], 1)
+    what = ("full {}-token request (all pairs + compose + seams)".format(int(tok)) if cold.all() else
+            "the cold bodies of request 0 ({} tokens, their pairs)".format(int(tok)))
     return {"value": tok * n_chains_sample / (wl.n_chains * dt), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{n_chains_sample} of {wl.n_chains} chains, full {int(tok)}-token request "
-                      f"(all pairs + compose + seams), {dt:.1f} s; scaled by chains"}
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "single_thread_value": tok / (wl.n_chains * dt1),
+            "sample": f"{n_chains_sample} of {wl.n_chains} chains, {what}, {dt:.1f} s on {threads} threads "
+                      f"(one chain on one thread: {dt1:.1f} s); scaled by chains"}
 
 
-def workload_text(name, wl, plan, C, d, w, req_tokens, n_build, hits, mode_name):
+def workload_text(name, wl, plan, C, d, w, req_tokens, n_build, hits, mode_name, layers=1):
     n_req = len(wl.requests)
     heads = "30 layers x 32 heads" if C == 960 else f"{C} heads"
     req = (f"one {req_tokens}-token request" if n_req == 1 else f"{n_req} requests, {req_tokens} tokens")
     if hits:
+        lay = f", per layer, {layers} layers" if layers > 1 else ", one layer"
         return (f"{wl.family} {wl.dtype}: build of {n_build} cold segment bodies + {mode_name} compose with w={w} "
-                f"seams over all {plan.n_slots} cached pairs: {C} chains ({heads}), d={d}, {req}")
+                f"seams over all {plan.n_slots} cached pairs: {C} chains ({heads}), d={d}, {req}{lay}")
     return (f"{wl.family} pair build + {mode_name} compose with w={w} seams: {C} chains ({heads}), d={d}, {req}, "
             f"{plan.n_slots} segments")
+
+
+def copy_bandwidth(stream, gib=2, reps=5):
+    """A plain device-to-device copy of `gib` GiB, timed with events:
+    (read + write bytes) / time, the best of `reps`."""
+    n = gib * (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = 0.0
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+        b.synchronize()
+        best = max(best, 2 * n * 4 / (a.elapsed_time(b) * 1e-3))
+    del src, dst
+    torch.cuda.empty_cache()
+    return best
+
+
+def roof(bytes_, flops, t, bound=None):
+    hbm, mf = bytes_ / t, flops / t
+    if bound is None:
+        bound = "hbm" if bytes_ / HBM_PEAK >= flops / BF16_PEAK else "mfma"
+    r = ({"bound": "hbm", "achieved": hbm / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": hbm / HBM_PEAK}
+         if bound == "hbm" else
+         {"bound": "mfma", "achieved": mf / 1e12, "peak": BF16_PEAK / 1e12, "unit": "TFLOP/s", "frac": mf / BF16_PEAK})
+    r.update({"alg_bytes": bytes_, "alg_flops": flops, "mfma_frac_alg": mf / BF16_PEAK, "hbm_frac_alg": hbm / HBM_PEAK})
+    return r
+
+
+class Layer:
+    """One layer's inputs, plan and buffers on the GPU, and the timed step."""
+
+    def __init__(self, config, layer, compose, stream):
+        dev = "cuda"
+        self.wl = wl = workloads.config(config, device=dev, layer=layer)
+        self.w = w = wl.w
+        self.plan = plan = request_plan(wl.requests, w, slot_order="longest_first")
+        d, C = wl.dk, wl.n_chains
+        self.stream = stream
+        self.L = L = hy.layout(wl.family, wl.dtype, C, d)
+        self.x = x = hy.tokens(wl.q, wl.k, wl.v, wl.g, wl.beta, wl.gamma)
+        te = hy.hypic_t_elems(wl.family, d)
+        self.T = torch.empty(plan.n_slots, C, te, device=dev)
+        self.S = torch.empty(plan.n_slots, C, d, d, device=dev)
+        sb = torch.from_numpy(plan.seg_begin).to(dev)
+        se = torch.from_numpy(plan.seg_end).to(dev)
+        self.lo = torch.from_numpy(plan.list_off).to(dev)
+        self.pid = torch.from_numpy(plan.pair_id).to(dev)
+        self.seam = torch.from_numpy(plan.seam_begin).to(dev)
+        self.state = torch.zeros(plan.n_req, C, d, d, device=dev)
+        self.o = torch.zeros(len(plan.pair_id), w, C, d, device=dev)
+        # Workloads with cache hits time the build of the cold bodies only,
+        # into their own pair buffers, and compose over the full pair cache,
+        # which is built once beforehand (untimed); the others time the build
+        # of every segment.
+        self.cold = cold = (np.concatenate([c for c in wl.cold])[plan.seg_index] if wl.cold
+                            else np.ones(plan.n_slots, bool))  # per slot
+        self.hits = not cold.all()
+        if compose == "auto":
+            n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+            # with too few chains to fill the GPU the tree's parallel blocks pay
+            # from lists of 8 entries: 32 entries on 16 GLA chains (0.20 ms against
+            # 0.44), 8 entries on 8 RetNet chains (0.042 ms against 0.048)
+            self.mode = hy.TREE if self.hits or (plan.n_req * C < n_cu and plan.max_list_len >= 8) else hy.SEQ
+        else:
+            self.mode = hy.TREE if compose == "tree" else hy.SEQ
+        if self.hits:
+            hy.hypic_segment_build(L, x, plan.n_slots, sb, se, plan.max_seg_len, self.T, self.S, stream=stream)
+            idx = np.nonzero(cold)[0]
+            self.bsb = torch.from_numpy(plan.seg_begin[idx]).to(dev)
+            self.bse = torch.from_numpy(plan.seg_end[idx]).to(dev)
+            self.n_build = len(idx)
+            self.bT = torch.empty(self.n_build, C, te, device=dev)
+            self.bS = torch.empty(self.n_build, C, d, d, device=dev)
+            self.build_lens = plan.seg_end[idx] - plan.seg_begin[idx]
+        else:
+            self.bsb, self.bse, self.n_build, self.bT, self.bS = sb, se, plan.n_slots, self.T, self.S
+            self.build_lens = plan.seg_end - plan.seg_begin
+        self.max_build = int(self.build_lens.max())
+        self.nws = hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, plan.n_req, plan.max_list_len, w)
+        self.ws = torch.empty(max(self.nws, 1), dtype=torch.uint8, device=dev)
+
+    def step(self, ev=None, cmode=None):
+        cmode = self.mode if cmode is None else cmode
+        st, p = self.stream, self.plan
+        if ev:
+            ev[0].record(st)
+        hy.hypic_segment_build(self.L, self.x, self.n_build, self.bsb, self.bse, self.max_build, self.bT, self.bS,
+                               stream=st)
+        if ev:
+            ev[1].record(st)
+        self.state.zero_()
+        if ev:
+            ev[2].record(st)
+        tree = cmode == hy.TREE
+        hy.hypic_compose(self.L, cmode, p.n_req, p.max_list_len, self.lo, self.pid, p.n_slots, self.T, self.S,
+                         self.x, self.seam, self.w, self.state, self.o, ws=self.ws if tree else None,
+                         ws_bytes=self.nws if tree else 0, stream=st)
+        if ev:
+            ev[3].record(st)
+
+    def timed(self, steps, cmode=None, libs=None):
+        """Median build and compose times (ms) over `steps` steps; with libs,
+        the steps alternate over the libraries and one pair of lists per
+        library comes back."""
+        libs = libs or [None]
+        evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)] for _ in libs]
+        for i in range(steps):
+            for li, lib in enumerate(libs):
+                if lib is not None:
+                    hy.hypic.use(lib)
+                self.step(evs[li][i], cmode)
+        torch.cuda.synchronize()
+        res = []
+        for ev in evs:
+            res.append((np.array([e[0].elapsed_time(e[1]) for e in ev]), np.array([e[2].elapsed_time(e[3]) for e in ev])))
+        return res
 
 
 def main():
@@ -176,11 +365,17 @@ def main():
                     help="only run a plain device-to-device copy of MIB MiB (5 times), to scale HBM counters")
     ap.add_argument("--compose", choices=("auto", "seq", "tree"), default="auto",
                     help="compose mode; auto: the tree scan where the workload asks for it (cache hits) or where the "
-                         "request's chains are fewer than the compute units and its list has at least 16 entries "
+                         "request's chains are fewer than the compute units and its list has at least 8 entries "
                          "(latency-bound), else sequential")
     ap.add_argument("--cpu-chains", type=int, default=-1,
                     help="chains in the oracle's CPU-baseline sample (-1: four per host thread, about 13 s of "
                          "host work at the default workload; 0: skip)")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="layers to run one after another, each on fresh inputs generated untimed (workloads "
+                         "with cache hits); the per-layer times and their sum are reported")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the fused cold prefill leg")
+    ap.add_argument("--ab", default=None, metavar="LIB",
+                    help="another build of libhypic.so: steps alternate between the two in this process")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path shards by chain with no "
@@ -199,122 +394,51 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calib_copy_bytes_read": n * 4, "calib_copy_bytes_written": n * 4, "launches": 5}))
         return
-    hy.load()
-
-    wl = workloads.config(args.config, device="cuda")
-    w = wl.w
-    plan = request_plan(wl.requests, w, slot_order="longest_first")
-    d, C = wl.dk, wl.n_chains
-    dev = "cuda"
-    L = hy.layout(wl.family, wl.dtype, C, d)
-    x = hy.tokens(wl.q, wl.k, wl.v, wl.g, wl.beta, wl.gamma)
-    te = hy.hypic_t_elems(wl.family, d)
-    T = torch.empty(plan.n_slots, C, te, device=dev)
-    S = torch.empty(plan.n_slots, C, d, d, device=dev)
-    sb = torch.from_numpy(plan.seg_begin).to(dev)
-    se = torch.from_numpy(plan.seg_end).to(dev)
-    lo = torch.from_numpy(plan.list_off).to(dev)
-    pid = torch.from_numpy(plan.pair_id).to(dev)
-    seam = torch.from_numpy(plan.seam_begin).to(dev)
-    state = torch.zeros(plan.n_req, C, d, d, device=dev)
-    o = torch.zeros(len(plan.pair_id), w, C, d, device=dev)
+    lib_a = hy.load()
+    libs = None
+    if args.ab:
+        libs = [lib_a, hy.hypic.load(os.path.abspath(args.ab), cache=False)]
     stream = torch.cuda.current_stream()
-    # Workloads with cache hits (n_cold set) time the build of the cold
-    # segment bodies only, into their own pair buffers, and compose with the
-    # associative tree scan over the full pair cache, which is built once
-    # beforehand (untimed); the others time the build of every segment and
-    # the sequential compose.
-    cold = (np.concatenate([c for c in wl.cold])[plan.seg_index] if wl.cold
-            else np.ones(plan.n_slots, bool))  # per slot
-    hits = not cold.all()
-    if args.compose == "auto":
-        n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
-        # with too few chains to fill the GPU the tree's parallel blocks pay
-        # from lists of 8 entries: 32 entries on 16 GLA chains (0.20 ms against
-        # 0.44), 8 entries on 8 RetNet chains (0.042 ms against 0.048)
-        mode = hy.TREE if hits or (plan.n_req * C < n_cu and plan.max_list_len >= 8) else hy.SEQ
-    else:
-        mode = hy.TREE if args.compose == "tree" else hy.SEQ
-    if hits:
-        hy.hypic_segment_build(L, x, plan.n_slots, sb, se, plan.max_seg_len, T, S, stream=stream)
-        cb_idx = np.nonzero(cold)[0]
-        bsb = torch.from_numpy(plan.seg_begin[cb_idx]).to(dev)
-        bse = torch.from_numpy(plan.seg_end[cb_idx]).to(dev)
-        n_build = len(cb_idx)
-        bT = torch.empty(n_build, C, te, device=dev)
-        bS = torch.empty(n_build, C, d, d, device=dev)
-        build_lens = plan.seg_end[cb_idx] - plan.seg_begin[cb_idx]
-    else:
-        bsb, bse, n_build, bT, bS = sb, se, plan.n_slots, T, S
-        build_lens = plan.seg_end - plan.seg_begin
-    max_build = int(build_lens.max())
-    nws = hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, plan.n_req, plan.max_list_len, w)
-    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    copy_bw = copy_bandwidth(stream)
 
-    def step(ev=None, cmode=mode):
-        if ev:
-            ev[0].record(stream)
-        hy.hypic_segment_build(L, x, n_build, bsb, bse, max_build, bT, bS, stream=stream)
-        if ev:
-            ev[1].record(stream)
-        state.zero_()
-        if ev:
-            ev[2].record(stream)
-        hy.hypic_compose(L, cmode, plan.n_req, plan.max_list_len, lo, pid, plan.n_slots, T, S, x, seam, w, state,
-                         o, ws=ws if cmode == hy.TREE else None, ws_bytes=nws if cmode == hy.TREE else 0,
-                         stream=stream)
-        if ev:
-            ev[3].record(stream)
-
+    lay = Layer(args.config, 0, args.compose, stream)
+    wl, plan, w, mode = lay.wl, lay.plan, lay.w, lay.mode
+    d, C = wl.dk, wl.n_chains
     for _ in range(args.warmup):
-        step()
+        lay.step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
+    (b_ms, c_ms), *ab = lay.timed(args.steps, libs=libs)
     wall = time.perf_counter() - t0
+    step_ms = wall * 1e3 / (args.steps * (2 if libs else 1))
+    hy.hypic.use(lib_a)
     # the other compose mode on the same lists, for comparison
     alt_mode = hy.SEQ if mode == hy.TREE else hy.TREE
-    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(sev[i], alt_mode)
-    torch.cuda.synchronize()
-    alt_ms = float(np.median([e[2].elapsed_time(e[3]) for e in sev]))
-    b_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    c_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
-    step_ms = wall * 1e3 / args.steps
+    (_, alt_c), = lay.timed(args.steps, alt_mode)
 
     in_bytes = 2 if wl.dtype == "bf16" else 4
     req_tokens = int(sum(int(b[-1] - b[0]) for b in wl.requests))
-    build_tokens = int(build_lens.sum())
-    bf, bb = build_cost(wl.family, build_lens, d, C, in_bytes)
+    build_tokens = int(lay.build_lens.sum())
+    bf, bb = build_cost(wl.family, lay.build_lens, d, C, in_bytes)
     n_seams = int((plan.seam_begin >= 0).sum())
     cf, cb = compose_cost(wl.family, len(plan.pair_id), n_seams, w, d, C, in_bytes)
     tb, tc = float(np.median(b_ms)) * 1e-3, float(np.median(c_ms)) * 1e-3
-    # the build's binding roof is the larger of its HBM and bf16-MFMA times
-    b_hbm, b_mfma = bb / tb, bf / tb
-    b_bound = "hbm" if bb / HBM_PEAK >= bf / BF16_PEAK else "mfma"
-    roof_build = ({"bound": "hbm", "achieved": b_hbm / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                   "frac": b_hbm / HBM_PEAK} if b_bound == "hbm" else
-                  {"bound": "mfma", "achieved": b_mfma / 1e12, "peak": BF16_PEAK / 1e12, "unit": "TFLOP/s",
-                   "frac": b_mfma / BF16_PEAK})
+    roof_build = roof(bb, bf, tb)
     bk_name, bk_files = build_kernel(wl.family, wl.dtype)
     key = "" if args.config == "c4" else "_" + args.config  # stored counters per workload
-    roof_build.update({"traffic": measured_traffic("build" + key, bk_files),
-                       "kernel": bk_name, "alg_bytes": bb, "alg_flops": bf,
-                       "mfma_frac_alg": b_mfma / BF16_PEAK, "hbm_frac_alg": b_hbm / HBM_PEAK})
-    ck_name, ck_files = compose_kernel(wl.family, wl.dtype == "bf16", d)
-    if mode == hy.TREE:
-        ck_name = "k_compose_dense (tree block phase) + k_tree_scan + k_tree_fix"
-    roof_comp = {"bound": "hbm", "achieved": cb / tc / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                 "frac": cb / tc / HBM_PEAK, "traffic": measured_traffic("compose" + key, ck_files),
-                 "kernel": ck_name, "alg_bytes": cb,
-                 "alg_flops": cf}
+    roof_build.update({"traffic": measured_traffic("build" + key, bk_files), "kernel": bk_name,
+                       "measured_copy_GBps": copy_bw / 1e9, "frac_of_measured_copy": bb / tb / copy_bw})
+    tree = mode == hy.TREE
+    ck_name, ck_files = compose_kernel(wl.family, wl.dtype == "bf16", d, tree)
+    roof_comp = roof(cb, cf, tc, "hbm")
+    roof_comp.update({"traffic": None if tree else measured_traffic("compose" + key, ck_files), "kernel": ck_name,
+                      "frac_of_measured_copy": cb / tc / copy_bw})
+    # value: request tokens per second of build (all chains); with cache hits
+    # only the cold bodies are built, and value counts those tokens
+    v_tokens = build_tokens if lay.hits else req_tokens
     out = {
         "metric": METRIC,
-        "value": build_tokens / tb,
+        "value": v_tokens / tb,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -325,11 +449,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": workload_text(args.config, wl, plan, C, d, w, req_tokens, n_build, hits,
-                                               "tree" if mode == hy.TREE else "seq"),
+        "config": {"workload": workload_text(args.config, wl, plan, C, d, w, req_tokens, lay.n_build, lay.hits,
+                                               "tree" if tree else "seq", args.layers),
                    "chains": C, "d": d, "request_tokens": req_tokens, "segments": plan.n_slots, "w": w,
-                   "built_segments": n_build, "built_tokens": build_tokens, "compose_mode": "tree" if mode == hy.TREE else "seq",
-                   "state_dtype": "f32", "slot_order": "longest_first"},
+                   "built_segments": lay.n_build, "built_tokens": build_tokens,
+                   "value_tokens": "cold body tokens" if lay.hits else "request tokens (seam tokens included)",
+                   "compose_mode": "tree" if tree else "seq", "state_dtype": "f32", "slot_order": "longest_first"},
         "build_ms": float(np.median(b_ms)),
         "build_ms_p10_p90": [float(np.percentile(b_ms, 10)), float(np.percentile(b_ms, 90))],
         "compose_latency_ms": float(np.median(c_ms)),
@@ -337,12 +462,66 @@ def main():
         "chain_tokens_per_s_build": build_tokens * C / tb,
         "roofline": roof_build,
         "roofline_compose": roof_comp,
+        "compose_alt": {"mode": "tree" if alt_mode == hy.TREE else "seq", "ms": float(np.median(alt_c))},
+        "hbm_copy_measured_GBps": copy_bw / 1e9,
     }
-    out["compose_alt"] = {"mode": "seq" if alt_mode == hy.SEQ else "tree", "ms": alt_ms}
+    if libs:
+        (bb_ms, cb_ms), = ab
+        out["ab"] = {"lib": args.ab, "build_ms": [float(np.median(b_ms)), float(np.median(bb_ms))],
+                     "compose_ms": [float(np.median(c_ms)), float(np.median(cb_ms))]}
+    # fused cold prefill of the same bodies (outputs of every body token and the pairs)
+    if not args.no_prefill and wl.family in ("deltanet", "gdn") and wl.dtype == "bf16":
+        pout = torch.empty(wl.n_tok, C, d, dtype=wl.k.dtype, device="cuda")
+        pT, pS = torch.empty_like(lay.bT), torch.empty_like(lay.bS)
+        pf = lambda: hy.hypic_segment_prefill(lay.L, lay.x, lay.n_build, lay.bsb, lay.bse, lay.max_build, pT, pS,
+                                              pout, stream=stream)
+        for _ in range(max(1, args.warmup)):
+            pf()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for e in evs:
+            e[0].record(stream)
+            pf()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        p_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+        tp = float(np.median(p_ms)) * 1e-3
+        pfl, pby = prefill_cost(wl.family, lay.build_lens, d, C, in_bytes)
+        rp = roof(pby, pfl, tp)
+        rp.update({"kernel": "k_build_dense_pipe (prefill instantiation)", "traffic": None})
+        out["prefill"] = {"ms": float(np.median(p_ms)), "ms_p10_p90": [float(np.percentile(p_ms, 10)),
+                                                                        float(np.percentile(p_ms, 90))],
+                          "tokens_per_s": v_tokens / tp, "ms_over_build": tp / tb, "roofline": rp}
+        del pout, pT, pS
+        torch.cuda.empty_cache()
+    if args.layers > 1:
+        # every further layer on fresh inputs (generated and its pair cache
+        # built untimed), then its timed steps; the first layer is the one above
+        per_b, per_c = [float(np.median(b_ms))], [float(np.median(c_ms))]
+        toks = [build_tokens]
+        del lay
+        torch.cuda.empty_cache()
+        for layer in range(1, args.layers):
+            ly = Layer(args.config, layer, args.compose, stream)
+            ly.step()
+            torch.cuda.synchronize()
+            (bl, cl), = ly.timed(max(3, args.steps // 2))
+            per_b.append(float(np.median(bl)))
+            per_c.append(float(np.median(cl)))
+            toks.append(int(ly.build_lens.sum()))
+            print(f"layer {layer}: build {per_b[-1]:.3f} ms, compose {per_c[-1]:.3f} ms", file=sys.stderr, flush=True)
+            del ly
+            torch.cuda.empty_cache()
+        out["layers"] = {"n": args.layers, "build_ms": per_b, "compose_ms": per_c,
+                         "build_ms_sum": float(np.sum(per_b)), "compose_ms_sum": float(np.sum(per_c)),
+                         "total_ms_sum": float(np.sum(per_b) + np.sum(per_c)),
+                         "build_tokens_per_s_all_layers": float(np.sum(toks)) / (np.sum(per_b) * 1e-3)}
+        lay = None
     if args.cpu_chains != 0:
         import oracle
         n_cpu = 4 * oracle.max_threads() if args.cpu_chains < 0 else args.cpu_chains
-        out["cpu_baseline"] = cpu_baseline(wl, min(n_cpu, C), w)
+        if lay is None:
+            lay = Layer(args.config, 0, args.compose, stream)
+        out["cpu_baseline"] = cpu_baseline(lay.wl, lay.plan, lay.cold, min(n_cpu, C), w)
     print(json.dumps(out), flush=True)
 
 

@@ -152,6 +152,26 @@ int hypic_segment_build(const hypic_layout *L, const hypic_tokens *x, int32_t n_
                         float *d_T, float *d_S, void *d_ws, size_t ws_bytes, void *stream);
 
 /*
+ * hypic_segment_prefill -- the fused cold prefill of segment bodies: in one
+ * chunked pass, every token's output and the segment's cached pair
+ * (codernav.top, linear layers: the pair is cached at the segment's first
+ * prefill; results: building it costs a few percent of that forward).
+ * Segment s covers tokens [d_seg_begin[s], d_seg_end[s]) and is read from a
+ * zero state, so its outputs are those of the position-independent body:
+ *   o_t = S_t^T q_t,  S_t the state after token t of the segment from S = 0,
+ * written to d_out[t * out_tok_stride + c * out_chain_stride + j] (j < dv) in
+ * the input dtype; d_T and d_S as hypic_segment_build writes them.  q is
+ * required.  Implemented for DeltaNet and GDN with bf16 inputs
+ * (HYPIC_E_UNSUPPORTED otherwise).  Every chunk of 64 tokens must keep its
+ * total log-decay above about -80 (the chunk form scales the solved rows by
+ * the chunk's decay).  d_out must not overlap the inputs or the pair.
+ */
+int hypic_segment_prefill(const hypic_layout *L, const hypic_tokens *x, int32_t n_seg,
+                          const int64_t *d_seg_begin, const int64_t *d_seg_end, int64_t max_seg_len,
+                          float *d_T, float *d_S, void *d_out, int64_t out_tok_stride,
+                          int64_t out_chain_stride, void *stream);
+
+/*
  * hypic_compose -- assemble request states from cached pairs
  * (codernav.top, linear layers: reuse left-multiplies T_C, then adds S(C|0);
  * seam windows: the linear layers advance the running state through each

@@ -283,7 +283,7 @@ int hypic_segment_build(const hypic_layout *L, const hypic_tokens *x, int32_t n_
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (validate_on() && (rc = validate_segments(n_seg, d_seg_begin, d_seg_end, max_seg_len, st))) return rc;
     if ((rc = injected("build"))) return rc;
-    hy::BuildArgs a;
+    hy::BuildArgs a{};
     a.x = to_tok(x);
     a.n_chains = L->n_chains;
     a.dk = L->dk;
@@ -380,6 +380,40 @@ int compose_call(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t max
 }  // namespace
 
 extern "C" {
+
+int hypic_segment_prefill(const hypic_layout *L, const hypic_tokens *x, int32_t n_seg, const int64_t *d_seg_begin,
+                          const int64_t *d_seg_end, int64_t max_seg_len, float *d_T, float *d_S, void *d_out,
+                          int64_t out_tok_stride, int64_t out_chain_stride, void *stream) {
+    int rc = check_layout(L);
+    if (rc) return rc;
+    if ((rc = check_tokens(L, x, true))) return rc;
+    if (n_seg < 0) return fail(HYPIC_E_INVALID, "n_seg < 0");
+    if (max_seg_len < 0) return fail(HYPIC_E_INVALID, "max_seg_len < 0");
+    if (out_chain_stride < L->dv || out_tok_stride < L->dv)
+        return fail(HYPIC_E_INVALID, "output strides (%lld, %lld) below dv", (long long)out_tok_stride,
+                    (long long)out_chain_stride);
+    if (!(L->family == HYPIC_DELTANET || L->family == HYPIC_GDN) || L->in_dtype != HYPIC_BF16)
+        return fail(HYPIC_E_UNSUPPORTED, "fused prefill is implemented for DeltaNet and GDN with bf16 inputs");
+    if (n_seg == 0) return ok();
+    if (!d_seg_begin || !d_seg_end || !d_T || !d_S || !d_out)
+        return fail(HYPIC_E_INVALID, "NULL segment or output pointer");
+    if ((int64_t)n_seg * L->n_chains > 0x7fffffff) return fail(HYPIC_E_INVALID, "n_seg * n_chains too large");
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (validate_on() && (rc = validate_segments(n_seg, d_seg_begin, d_seg_end, max_seg_len, st))) return rc;
+    if ((rc = injected("build"))) return rc;
+    hy::BuildArgs a{};
+    a.x = to_tok(x);
+    a.n_chains = L->n_chains;
+    a.dk = L->dk;
+    a.seg_begin = d_seg_begin;
+    a.seg_end = d_seg_end;
+    a.T = d_T;
+    a.S = d_S;
+    a.o = d_out;
+    a.ots = out_tok_stride;
+    a.ocs = out_chain_stride;
+    return launched(hy::build_dense_pipe(a, L->family, padded_d(L->dk), n_seg, st), "prefill launch");
+}
 
 int hypic_compose(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t max_list_len, const int32_t *d_list_off,
                   const int32_t *d_pair_id, int64_t n_slots, const float *d_T, const float *d_S,

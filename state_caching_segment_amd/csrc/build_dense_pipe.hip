@@ -42,22 +42,30 @@ namespace hy {
 
 typedef short s4 __attribute__((ext_vector_type(4)));
 
-template <int D>
+// PF (prefill): the chunk's Q rows and the lower blocks of tril(Q K^T) are
+// staged too, and V is staged as bf16 V^T with the per-token decays apart
+// (ev = e^{Gamma_c - Gamma_t}, eo = e^{Gamma_t}, ei = e^{Gamma_t - Gamma_c}),
+// which makes room for them.
+template <int D, bool PF = false>
 struct PipeCfg {
     static constexpr int NC = 2 * D / 32;  // carry waves
     static constexpr int NT = (NC + 2) * 64;
     static constexpr int RT = D / 16;
     static constexpr int KB = D / 32;
-    static constexpr int LDK = D + 8;   // bf16 row stride of K rows
+    static constexpr int LDK = D + 8;   // bf16 row stride of K (and Q) rows
     static constexpr int LDV = CH + 4;  // fp32 row stride of (E V)^T
+    static constexpr int LDVB = CH + 8; // bf16 row stride of V^T (PF)
     static constexpr int LDT = 20;      // fp32 row stride of a diagonal block of N0
     static constexpr int TILE = 512;    // bf16 per pre-split 16 x 16 tile: [row][4 col groups][hi 4 | lo 4]
     static constexpr int al(int x) { return (x + 15) / 16 * 16; }
-    // one buffer: K rows, (E V)^T, A_b, -M_bc, lambda
+    // one buffer: K rows, [Q rows], (E V)^T or V^T and the decays, A_b, -M_bc, lambda
     static constexpr int bK = 0;
-    static constexpr int bV = bK + al(CH * LDK * 2);
-    static constexpr int bA = bV + al(D * LDV * 4);
-    static constexpr int bM = bA + 4 * TILE * 2;
+    static constexpr int bQ = bK + al(CH * LDK * 2);
+    static constexpr int bV = PF ? bQ + al(CH * LDK * 2) : bQ;
+    static constexpr int bE = bV + (PF ? al(D * LDVB * 2) : al(D * LDV * 4));
+    static constexpr int bA = bE + (PF ? 3 * CH * 4 : 0);
+    static constexpr int bQK = bA + 4 * TILE * 2;  // (PF) the ten lower 16 x 16 blocks of tril(Q K^T), pre-split
+    static constexpr int bM = bQK + (PF ? 10 * TILE * 2 : 0);
     static constexpr int bLam = bM + 6 * TILE * 2;
     static constexpr int BUF = al(bLam + 16);
     // factor-wave scratch: beta, diagonal blocks of N0, their inverses (pre-split)
@@ -131,12 +139,75 @@ __device__ __forceinline__ void wave_lds_fence() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D, int FAM>
+// PF: fused cold prefill.  Besides the pair, every token's output of the
+// segment read from a zero state, o_t = S_t^T q_t, written in bf16 to a.o.
+// Within a chunk that starts from S0, with u_i the i-th row of the decayed
+// solve (R'_i = e^{Gamma_c - Gamma_i} u_i),
+//     S_t = e^{Gamma_t} S0 + sum_{i<=t} e^{Gamma_t - Gamma_i} k_i u_i^T,
+// so  O = diag(e^{Gamma_t}) Q S0 + diag(e^{Gamma_t - Gamma_c}) tril(Q K^T) R'
+// (tril inclusive): each S wave forms its 32 columns of O on the matrix cores
+// after its block solve, before the carry update.
+// One S wave's 32 output columns (c0 .. c0+31 of o) for the chunk of tokens
+// t0 .. t0 + min(L, 64) - 1, from the chunk-start state X (its S columns), the
+// solved R' (split, C layout per 16-row block) and the staged blocks of
+// tril(Q K^T); one 16-column half at a time, which bounds the registers held.
+template <int D, typename Cfg>
+__device__ __forceinline__ void prefill_out(const f32x4 (&X)[D / 16][2], const s4 (&Rh)[4][2], const s4 (&Rl)[4][2],
+                                            const char *buf, const BuildArgs &a, int64_t t0, int L, int chain, int c0) {
+    constexpr int KB = D / 32, LDK = Cfg::LDK, TILE = Cfg::TILE;
+    const int lane = lane_fresh(), r16 = lane & 15, grp = lane >> 4;
+    const bf16 *bQ = reinterpret_cast<const bf16 *>(buf + Cfg::bQ);
+    const bf16 *bQK = reinterpret_cast<const bf16 *>(buf + Cfg::bQK);
+    const float *bE = reinterpret_cast<const float *>(buf + Cfg::bE);
+    bf16 *o = reinterpret_cast<bf16 *>(a.o) + (int64_t)chain * a.ocs + c0 + r16;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        // P = Q S0 on this half's columns (the state split hi + lo; q exact in bf16)
+        f32x4 P[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) P[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            bf16x8 xh, xl;
+            float xv[8];
+            acc_to_perm(X[2 * kb][nt], X[2 * kb + 1][nt], xv);
+            split8(xv, xh, xl);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const bf16x8 qh = lds_perm(bQ, LDK, 16 * mt + r16, 32 * kb, grp);
+                P[mt] = mfma(qh, xh, P[mt]);
+                P[mt] = mfma(qh, xl, P[mt]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            f32x4 oi = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ib = 0; ib <= tb; ++ib) {
+                s4 ch, cl;
+                tile_frag(bQK + (tb * (tb + 1) / 2 + ib) * TILE, r16, grp, ch, cl);
+                oi = mma16(ch, cl, Rh[ib][nt], Rl[ib][nt], oi);
+            }
+            const f32x4 eo = *reinterpret_cast<const f32x4 *>(bE + CH + 16 * tb + 4 * grp);
+            const f32x4 ei = *reinterpret_cast<const f32x4 *>(bE + 2 * CH + 16 * tb + 4 * grp);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int t = 16 * tb + 4 * grp + jj;
+                const float v = eo[jj] * P[tb][jj] + ei[jj] * oi[jj];
+                if (t < L && c0 + 16 * nt + r16 < a.dk) o[(t0 + t) * a.ots + 16 * nt] = (bf16)v;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+template <int D, int FAM, bool PF = false>
 __global__ void __launch_bounds__((2 * D / 32 + 2) * 64)
 k_build_dense_pipe(BuildArgs a) {
-    using Cfg = PipeCfg<D>;
+    using Cfg = PipeCfg<D, PF>;
     constexpr int NC = Cfg::NC, RT = Cfg::RT, KB = Cfg::KB;
-    constexpr int LDK = Cfg::LDK, LDV = Cfg::LDV, LDT = Cfg::LDT, TILE = Cfg::TILE;
+    constexpr int LDK = Cfg::LDK, LDV = Cfg::LDV, LDVB = Cfg::LDVB, LDT = Cfg::LDT, TILE = Cfg::TILE;
     constexpr float L2E = 1.4426950408889634f;
     __shared__ __attribute__((aligned(16))) char smem[Cfg::total];
 
@@ -153,7 +224,10 @@ k_build_dense_pipe(BuildArgs a) {
         // the factor waves go first at issue on the SIMDs they share with
         // carry waves: their chains of short dependent steps set the period
         __builtin_amdgcn_s_setprio(3);
-        const bool kw = wv == NC;  // K / factor wave, else V / gate wave
+        // each role is its own instantiation, so that neither holds the
+        // other's prefetch registers
+        auto role = [&](auto KWC) {
+        constexpr bool kw = decltype(KWC)::value;  // K / factor wave, else V / gate wave
         const int lane = tid & 63;
         const bf16 *src = reinterpret_cast<const bf16 *>(kw ? a.x.k : a.x.v) + (int64_t)chain * a.x.cs;
         const bf16 *gp = FAM == GDN ? reinterpret_cast<const bf16 *>(a.x.g) + (int64_t)chain * a.x.gcs : nullptr;
@@ -163,6 +237,7 @@ k_build_dense_pipe(BuildArgs a) {
         constexpr int RV = D / 8;
         bf16x8 pre[RV];
         bf16 spre = (bf16)0.f;
+        const bf16 *qsrc = PF ? reinterpret_cast<const bf16 *>(a.x.q) + (int64_t)chain * a.x.cs : nullptr;
         auto prefetch = [&](int c) {
             const int64_t c0 = (int64_t)c * CH;
             const int L = (int)(n - c0 < CH ? n - c0 : CH);
@@ -198,11 +273,23 @@ k_build_dense_pipe(BuildArgs a) {
                     gc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 63));
                 }
                 const float ec = __builtin_amdgcn_exp2f(gc - s);
-                float *bV = reinterpret_cast<float *>(buf + Cfg::bV);
+                if constexpr (PF) {
+                    bf16 *bV = reinterpret_cast<bf16 *>(buf + Cfg::bV);
 #pragma unroll
-                for (int p = 0; p < RV; ++p)
+                    for (int p = 0; p < RV; ++p)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) bV[(8 * p + e) * LDV + lane] = ec * (float)pre[p][e];
+                        for (int e = 0; e < 8; ++e) bV[(8 * p + e) * LDVB + lane] = pre[p][e];
+                    float *bE = reinterpret_cast<float *>(buf + Cfg::bE);
+                    bE[lane] = ec;
+                    bE[CH + lane] = __builtin_amdgcn_exp2f(s);
+                    bE[2 * CH + lane] = __builtin_amdgcn_exp2f(s - gc);
+                } else {
+                    float *bV = reinterpret_cast<float *>(buf + Cfg::bV);
+#pragma unroll
+                    for (int p = 0; p < RV; ++p)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) bV[(8 * p + e) * LDV + lane] = ec * (float)pre[p][e];
+                }
                 if (lane == 0) *reinterpret_cast<float *>(buf + Cfg::bLam) = __builtin_amdgcn_exp2f(gc);
                 return;
             }
@@ -215,7 +302,53 @@ k_build_dense_pipe(BuildArgs a) {
 #pragma unroll
             for (int p = 0; p < RV; ++p) *reinterpret_cast<bf16x8 *>(bK + lane * LDK + 8 * p) = pre[p];
             sB[lane] = (float)spre;
+            // (PF) this chunk's q rows, not fetched ahead: they are requested
+            // once the K rows are stored (the factor wave has slack in
+            // the chunk period; holding them two chunks ahead next to the K
+            // rows would not fit its registers)
+            bf16x8 preq[PF ? RV : 1];
+            if constexpr (PF) {
+                const int64_t c0 = (int64_t)c * CH;
+                const int L = (int)(n - c0 < CH ? n - c0 : CH);
+                const bool on = lane < L;
+                const bf16 *qrow = qsrc + (on ? b0 + c0 + lane : b0) * a.x.ts;
+#pragma unroll
+                for (int p = 0; p < RV; ++p) {
+                    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(qrow + 8 * (8 * p < dk ? p : 0));
+                    preq[p] = (on && 8 * p < dk) ? v : bf16x8{};
+                }
+            }
+            if constexpr (PF) {
+                bf16 *bQ = reinterpret_cast<bf16 *>(buf + Cfg::bQ);
+#pragma unroll
+                for (int p = 0; p < RV; ++p) *reinterpret_cast<bf16x8 *>(bQ + lane * LDK + 8 * p) = preq[p];
+            }
             wave_lds_fence();
+            if constexpr (PF) {
+                // block (tb, ib <= tb) of tril(Q K^T) as the A operand: the lane
+                // needs (Q K^T)[16 tb + r16][16 ib + 4 grp + e], which is where
+                // the C layout of K_ib Q_tb^T puts it (exact: bf16 products
+                // summed in fp32), split hi + lo
+                const bf16 *bQ = reinterpret_cast<const bf16 *>(buf + Cfg::bQ);
+                bf16 *bQK = reinterpret_cast<bf16 *>(buf + Cfg::bQK);
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+                    for (int ib = 0; ib <= tb; ++ib) {
+                        f32x4 cq = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int kb = 0; kb < KB; ++kb)
+                            cq = mfma(lds_cont(bK, LDK, 16 * ib + r16, 32 * kb, grp),
+                                      lds_cont(bQ, LDK, 16 * tb + r16, 32 * kb, grp), cq);
+                        if (ib == tb) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) cq[e] = (4 * grp + e <= r16) ? cq[e] : 0.f;
+                        }
+                        tile_put(bQK + (tb * (tb + 1) / 2 + ib) * TILE, r16, grp, cq);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
             // Gram tiles, one block row b at a time, in C layout: the lane holds
             // rows t = 16b + 4grp + e, column i = 16c + r16 of N0 = beta_t G_ti.
             // Diagonal blocks go to LDS row-major for the inverse; the six
@@ -306,6 +439,11 @@ k_build_dense_pipe(BuildArgs a) {
             }
             __syncthreads();
         }
+        };
+        if (wv == NC)
+            role(std::true_type{});
+        else
+            role(std::false_type{});
         return;
     }
 
@@ -359,7 +497,20 @@ k_build_dense_pipe(BuildArgs a) {
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 f32x4 y = -lam * Z[mt][nt];
-                if (isS) y += *reinterpret_cast<const f32x4 *>(bV + (cbase - D + 16 * nt + r16) * LDV + 16 * mt + 4 * grp);
+                if constexpr (PF) {
+                    if (isS) {
+                        const bf16x4 v4 = *reinterpret_cast<const bf16x4 *>(
+                            reinterpret_cast<const bf16 *>(buf + Cfg::bV) + (cbase - D + 16 * nt + r16) * LDVB + 16 * mt +
+                            4 * grp);
+                        const f32x4 e4 = *reinterpret_cast<const f32x4 *>(
+                            reinterpret_cast<const float *>(buf + Cfg::bE) + 16 * mt + 4 * grp);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) y[e] += e4[e] * (float)v4[e];
+                    }
+                } else {
+                    if (isS)
+                        y += *reinterpret_cast<const f32x4 *>(bV + (cbase - D + 16 * nt + r16) * LDV + 16 * mt + 4 * grp);
+                }
                 split4(y, Yh[mt][nt], Yl[mt][nt]);
             }
         // R'_b = A_b Y_b - sum_{c<b} M_bc R'_c, kept split
@@ -380,6 +531,10 @@ k_build_dense_pipe(BuildArgs a) {
             }
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) split4(r[nt], Rh[b][nt], Rl[b][nt]);
+        }
+        if constexpr (PF) {
+            if (isS) prefill_out<D, Cfg>(X, Rh, Rl, buf, a, b0 + (int64_t)c * CH, (int)(n - (int64_t)c * CH), chain,
+                                         cbase - D);
         }
         // X = lambda X + K^T R'
         if (FAM == GDN) {
@@ -426,7 +581,10 @@ k_build_dense_pipe(BuildArgs a) {
 template <int D, int FAM>
 static hipError_t launch_pipe(const BuildArgs &a, int n_seg, hipStream_t st) {
     const dim3 grid((unsigned)(n_seg * (int64_t)a.n_chains));
-    hipLaunchKernelGGL((k_build_dense_pipe<D, FAM>), grid, dim3(PipeCfg<D>::NT), 0, st, a);
+    if (a.o)
+        hipLaunchKernelGGL((k_build_dense_pipe<D, FAM, true>), grid, dim3(PipeCfg<D, true>::NT), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_build_dense_pipe<D, FAM, false>), grid, dim3(PipeCfg<D>::NT), 0, st, a);
     return hipGetLastError();
 }
 

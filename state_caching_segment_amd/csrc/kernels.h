@@ -15,6 +15,8 @@ struct BuildArgs {
     const int64_t *seg_end;
     float *T;  // [seg][chain][t_elems]
     float *S;  // [seg][chain][dk][dk]
+    void *o;   // fused prefill: per-token outputs o[t * ots + chain * ocs + j], in the input dtype; else null
+    int64_t ots, ocs;
 };
 
 struct ComposeArgs {

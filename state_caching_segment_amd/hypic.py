@@ -24,8 +24,8 @@ SEQ, TREE = 0, 1
 OP_BUILD, OP_COMPOSE_SEQ, OP_COMPOSE_TREE, OP_SEAM = 0, 1, 2, 3
 STATUS = {0: "HYPIC_OK", -1: "HYPIC_E_INVALID", -2: "HYPIC_E_UNSUPPORTED", -3: "HYPIC_E_WORKSPACE",
           -4: "HYPIC_E_DEVICE"}
-EXPORTS = ("hypic_t_elems", "hypic_workspace_bytes", "hypic_segment_build", "hypic_compose",
-           "hypic_compose_tree_noalloc", "hypic_seam_advance", "hypic_status_string", "hypic_last_error")
+EXPORTS = ("hypic_t_elems", "hypic_workspace_bytes", "hypic_segment_build", "hypic_segment_prefill",
+           "hypic_compose", "hypic_compose_tree_noalloc", "hypic_seam_advance", "hypic_status_string", "hypic_last_error")
 NOALLOC_WORKSPACE_BYTES = 64 << 20  # HYPIC_NOALLOC_WORKSPACE_BYTES
 
 
@@ -51,10 +51,12 @@ class hypic_tokens(ctypes.Structure):
 _lib = None
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libhypic.so from the package directory (raises if it is not built)."""
+def load(path: str = LIB_PATH, cache: bool = True) -> ctypes.CDLL:
+    """Load libhypic.so from the package directory (raises if it is not built).
+    cache=False loads another build of the library (e.g. for a same-process
+    A/B timing) without making it the one the calls below use."""
     global _lib
-    if _lib is not None:
+    if cache and _lib is not None:
         return _lib
     if not os.path.exists(path):
         raise ImportError(f"libhypic is not built ({path} missing); run __graft_entry__.build()")
@@ -66,6 +68,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hypic_workspace_bytes.restype = sz
     lib.hypic_segment_build.argtypes = [P, P, i32, P, P, i64, P, P, P, sz, P]
     lib.hypic_segment_build.restype = ctypes.c_int
+    lib.hypic_segment_prefill.argtypes = [P, P, i32, P, P, i64, P, P, P, i64, i64, P]
+    lib.hypic_segment_prefill.restype = ctypes.c_int
     lib.hypic_compose.argtypes = [P, i32, i32, i32, P, P, i64, P, P, P, P, i32, P, P, P, P, sz, P]
     lib.hypic_compose.restype = ctypes.c_int
     lib.hypic_compose_tree_noalloc.argtypes = [P, i32, i32, P, P, i64, P, P, P, P, i32, P, P, P, P]
@@ -76,8 +80,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hypic_status_string.restype = ctypes.c_char_p
     lib.hypic_last_error.argtypes = []
     lib.hypic_last_error.restype = ctypes.c_char_p
-    _lib = lib
+    if cache:
+        _lib = lib
     return lib
+
+
+def use(lib: ctypes.CDLL) -> None:
+    """Route the calls below to `lib` (a library returned by load)."""
+    global _lib
+    _lib = lib
 
 
 def _p(t) -> Optional[int]:
@@ -132,6 +143,15 @@ def hypic_segment_build(L: hypic_layout, x: hypic_tokens, n_seg: int, seg_begin,
                         T, S, ws=None, ws_bytes: int = 0, stream=None) -> None:
     _check(load().hypic_segment_build(ctypes.byref(L), ctypes.byref(x), n_seg, _p(seg_begin), _p(seg_end),
                                       int(max_seg_len), _p(T), _p(S), _p(ws), ws_bytes, _stream(stream)))
+
+
+def hypic_segment_prefill(L: hypic_layout, x: hypic_tokens, n_seg: int, seg_begin, seg_end, max_seg_len: int,
+                          T, S, out, stream=None) -> None:
+    """out: token-major [token][chain][dv] tensor (any strides with a contiguous
+    feature axis) in the input dtype."""
+    _check(load().hypic_segment_prefill(ctypes.byref(L), ctypes.byref(x), n_seg, _p(seg_begin), _p(seg_end),
+                                        int(max_seg_len), _p(T), _p(S), _p(out), out.stride(0), out.stride(1),
+                                        _stream(stream)))
 
 
 def hypic_compose(L: hypic_layout, mode: int, n_req: int, max_list_len: int, list_off, pair_id, n_slots: int,
