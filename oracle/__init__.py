@@ -64,6 +64,9 @@ def _load():
         lib.oracle_request_batch.argtypes = [i32, i32, i32, i32, i64, i32, P, i32, P, P, P, P, P, P,
                                              P, P, P, P, i32]
         lib.oracle_gate_dim.argtypes = [i32, i32]
+        lib.oracle_rope_matrix.argtypes = [i32, f64, f64, P]
+        lib.oracle_rerotate.argtypes = [i32, i32, P, P, P, P, P]
+        lib.oracle_conv.argtypes = [i64, i32, i32, P, P, i32, P]
         lib.oracle_max_threads.argtypes = []
         _lib = lib
     return _lib
@@ -177,3 +180,33 @@ def rel_fro(x, ref) -> float:
     nr = np.linalg.norm(ref)
     d = np.linalg.norm(x - ref)
     return float(d / nr) if nr > 0 else float(d)
+
+
+# ---- variant patches (codernav.top, linear layers, last paragraph) ----------
+
+def rope_matrix(d: int, p: float, base: float = 10000.0) -> np.ndarray:
+    """R(p): channels (i, i + d/2) rotated by p * base^(-2i/d), as a d x d matrix."""
+    R = np.zeros((d, d))
+    _load().oracle_rope_matrix(d, float(p), float(base), _ptr(R))
+    return R
+
+
+def rerotate(T, S, p: float, base: float = 10000.0) -> Tuple[np.ndarray, np.ndarray]:
+    """A pair cached at local positions, moved to offset p: (R T R^T, R S)."""
+    T, S = _f64(T), _f64(S)
+    dk, dv = S.shape
+    R = rope_matrix(dk, p, base)
+    To, So = np.zeros((dk, dk)), np.zeros((dk, dv))
+    _load().oracle_rerotate(dk, dv, _ptr(R), _ptr(T), _ptr(S), _ptr(To), _ptr(So))
+    return To, So
+
+
+def conv(x, w, act: int = 0) -> np.ndarray:
+    """Causal depthwise convolution of raw inputs x [n][d] with taps w [d][K]
+    (zero before token 0); act 0: none, 1: SiLU."""
+    x, w = _f64(x), _f64(w)
+    n, d = x.shape
+    y = np.zeros((n, d))
+    _load().oracle_conv(n, d, w.shape[1], _ptr(x), _ptr(w), int(act), _ptr(y))
+    return y
+

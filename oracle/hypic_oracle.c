@@ -268,3 +268,83 @@ int oracle_max_threads(void) {
     return 1;
 #endif
 }
+
+/*
+ * Variant patches (codernav.top article, section on linear layers, its last
+ * paragraph; xix.ai article, the end of the paragraph on linear layers): two
+ * model variants need a patch around the cached pair at reuse.
+ *
+ * Short causal convolution before the recurrence.  A depthwise convolution
+ * of K taps over a channel's raw inputs x (zero before the first token):
+ *     y_t = act( sum_{j=0}^{K-1} w[j] x_{t-K+1+j} )
+ * (act: identity, or SiLU z / (1 + e^-z)).  A seam token's taps reach back
+ * into the previous segment; the warm-up feeds them that segment's last K-1
+ * raw inputs, which is the whole-sequence convolution at those positions.
+ *
+ * Rotary position embeddings on the keys.  R(p) rotates each pair of
+ * channels (i, i + d/2), i < d/2, by the angle p * theta_i with
+ * theta_i = base^(-2i/d):
+ *     (R x)_i       = cos x_i - sin x_{i+d/2}
+ *     (R x)_{i+d/2} = sin x_i + cos x_{i+d/2}
+ * A segment cached with keys at local positions 0 .. n-1 and reused at offset
+ * P has keys R(P) R(local) k; the transitions that keys enter through become
+ * R(P) A_t R(P)^T when the decay commutes with R(P), so the re-rotated pair is
+ *     T' = R(P) T R(P)^T,   S' = R(P) S.
+ * These are plain matrix products here, with R(P) formed explicitly.
+ */
+
+/* R(p) as an explicit d x d matrix (d even), angles in fp64. */
+void oracle_rope_matrix(int d, double p, double base, double *R) {
+    int h = d / 2, i;
+    memset(R, 0, sizeof(double) * d * d);
+    for (i = 0; i < h; i++) {
+        double th = pow(base, -2.0 * i / d), a = p * th;
+        double c = cos(a), s = sin(a);
+        R[i * d + i] = c;
+        R[i * d + i + h] = -s;
+        R[(i + h) * d + i] = s;
+        R[(i + h) * d + i + h] = c;
+    }
+}
+
+/* T' = R T R^T (T dense dk x dk), S' = R S (dk x dv). */
+void oracle_rerotate(int dk, int dv, const double *R, const double *T, const double *S, double *Tout,
+                     double *Sout) {
+    int i, j, l;
+    double *A = (double *)malloc(sizeof(double) * dk * dk);
+    for (i = 0; i < dk; i++)
+        for (j = 0; j < dk; j++) {
+            double acc = 0.0;
+            for (l = 0; l < dk; l++) acc += R[i * dk + l] * T[l * dk + j];
+            A[i * dk + j] = acc;
+        }
+    for (i = 0; i < dk; i++)
+        for (j = 0; j < dk; j++) {
+            double acc = 0.0;
+            for (l = 0; l < dk; l++) acc += A[i * dk + l] * R[j * dk + l];
+            Tout[i * dk + j] = acc;
+        }
+    for (i = 0; i < dk; i++)
+        for (j = 0; j < dv; j++) {
+            double acc = 0.0;
+            for (l = 0; l < dk; l++) acc += R[i * dk + l] * S[l * dv + j];
+            Sout[i * dv + j] = acc;
+        }
+    free(A);
+}
+
+/* Causal depthwise convolution of one chain's raw inputs x [n][d] with
+ * taps w [d][K] (zero before token 0), act 0: none, 1: SiLU; y [n][d]. */
+void oracle_conv(int64_t n, int d, int K, const double *x, const double *w, int act, double *y) {
+    int64_t t;
+    int c, j;
+    for (t = 0; t < n; t++)
+        for (c = 0; c < d; c++) {
+            double z = 0.0;
+            for (j = 0; j < K; j++) {
+                int64_t u = t - K + 1 + j;
+                if (u >= 0) z += w[c * K + j] * x[u * d + c];
+            }
+            y[t * d + c] = act == 1 ? z / (1.0 + exp(-z)) : z;
+        }
+}
