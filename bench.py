@@ -265,6 +265,51 @@ def roof(bytes_, flops, t, bound=None):
     return r
 
 
+def _median_ms(fn, steps, stream):
+    fn()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in evs:
+        e[0].record(stream)
+        fn()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+
+
+def variant_leg(lay, steps, stream):
+    """Times of the variant patches on the layer's shapes, with their HBM
+    rooflines: re-rotation reads and writes every pair once; the warm-up
+    reads K - 1 + w raw tokens and writes w tokens of q, k, v per window."""
+    wl, plan = lay.wl, lay.plan
+    d, C, w, K = wl.dk, wl.n_chains, lay.w, 4
+    res = {}
+    in_bytes = 2 if wl.dtype == "bf16" else 4
+    if wl.family not in ("gla", "kda"):
+        te = hy.hypic_t_elems(wl.family, d)
+        Tr, Sr = torch.empty_like(lay.T), torch.empty_like(lay.S)
+        ident = torch.arange(plan.n_slots, dtype=torch.int32, device="cuda")
+        offs = torch.from_numpy(plan.seg_begin).cuda()
+        ms = _median_ms(lambda: hy.hypic_rerotate(lay.L, plan.n_slots, ident, offs, 10000.0, lay.T, lay.S, Tr, Sr,
+                                                  stream=stream), steps, stream)
+        byts = 2.0 * plan.n_slots * C * (te + d * d) * 4
+        res["rerotate"] = {"ms": ms, "pairs": plan.n_slots * C,
+                           "roofline": roof(byts, 0.0, ms * 1e-3, "hbm") | {"kernel": "k_rerotate"}}
+        del Tr, Sr
+    seams = plan.seam_begin[plan.seam_begin >= 0]
+    if len(seams):
+        ns = len(seams)
+        outs = [torch.empty(ns, w, C, d, dtype=wl.k.dtype, device="cuda") for _ in range(3)]
+        taps = torch.randn(3, C, d, K, device="cuda") / K
+        sb = torch.from_numpy(seams).cuda()
+        raw = hy.tokens(q=wl.q, k=wl.k, v=wl.v)
+        ms = _median_ms(lambda: hy.hypic_conv_warmup(lay.L, raw, taps, K, 1, ns, sb, w, *outs, stream=stream),
+                        steps, stream)
+        byts = ns * C * 3.0 * d * in_bytes * (K - 1 + 2 * w) + 3 * C * d * K * 4
+        res["conv_warmup"] = {"ms": ms, "windows": ns * C, "taps": K,
+                              "roofline": roof(byts, 0.0, ms * 1e-3, "hbm") | {"kernel": "k_conv_warmup"}}
+    return res
+
+
 class Layer:
     """One layer's inputs, plan and buffers on the GPU, and the timed step."""
 
@@ -493,6 +538,11 @@ def main():
                           "tokens_per_s": v_tokens / tp, "ms_over_build": tp / tb, "roofline": rp}
         del pout, pT, pS
         torch.cuda.empty_cache()
+    # variant patches at this shape: every cached pair re-rotated to its body's
+    # absolute offset (rotary embeddings), and the seam windows' convolved
+    # q, k, v from raw inputs (short convolution, 4 taps, SiLU)
+    if not args.no_prefill:
+        out["variants"] = variant_leg(lay, args.steps, stream)
     if args.layers > 1:
         # every further layer on fresh inputs (generated and its pair cache
         # built untimed), then its timed steps; the first layer is the one above

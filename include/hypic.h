@@ -59,8 +59,8 @@
  *     token count is not an argument, so token indices are checked for sign
  *     only.  The detail of the last error on the calling thread is in
  *     hypic_last_error().  On error the outputs are unspecified.
- *   - HYPIC_FAULT_INJECT ("1" or "all"; or "build", "compose", "seam" for one
- *     call): after its arguments have been validated, the call returns
+ *   - HYPIC_FAULT_INJECT ("1" or "all"; or "build", "compose", "seam",
+ *     "rerotate", "conv" for one call): after its arguments have been validated, the call returns
  *     HYPIC_E_DEVICE and enqueues nothing.  For testing callers' error paths.
  *   - dv must equal dk (HYPIC_E_UNSUPPORTED otherwise): every kernel keeps the
  *     state and T in tiles of the same width, and every workload these
@@ -243,6 +243,49 @@ int hypic_compose_tree_noalloc(const hypic_layout *L, int32_t n_req, int32_t max
 int hypic_seam_advance(const hypic_layout *L, const hypic_tokens *x, int32_t n_items,
                        const int64_t *d_tok_begin, int32_t w, float *d_state, float *d_o,
                        void *stream);
+
+/*
+ * hypic_rerotate -- move cached pairs to the absolute offsets they are reused
+ * at, for models with rotary position embeddings on the keys (codernav.top,
+ * linear layers, last paragraph: state re-rotation; xix.ai, paragraph on
+ * linear layers).  Rotation R(p): each channel pair (i, i + dk/2), i < dk/2,
+ * turns by p * rope_base^(-2i/dk):
+ *     (R x)_i = cos x_i - sin x_{i+dk/2},   (R x)_{i+dk/2} = sin x_i + cos x_{i+dk/2}
+ * (angles formed in fp64).  A pair built with the segment's keys at local
+ * positions 0, 1, ... and reused with its first token at position p is then
+ *     T' = R(p) T R(p)^T  (a scalar T is unchanged),   S' = R(p) S.
+ * Item i reads slot d_slot[i] of (d_T, d_S) and writes item i of
+ *   d_T_out [n_items][n_chains][t_elems], d_S_out [n_items][n_chains][dk][dv]
+ * at offset d_offset[i].  In place is allowed when d_T_out == d_T,
+ * d_S_out == d_S and d_slot[i] == i; no other overlap.  The law holds when
+ * the decay commutes with R(p): LINEAR, RETNET, MAMBA2, DELTANET, GDN.  GLA
+ * and KDA (per-channel gates) return HYPIC_E_UNSUPPORTED.  All pointers 16-byte
+ * aligned; rope_base > 1.
+ */
+int hypic_rerotate(const hypic_layout *L, int32_t n_items, const int32_t *d_slot, const int64_t *d_offset,
+                   double rope_base, const float *d_T, const float *d_S, float *d_T_out, float *d_S_out,
+                   void *stream);
+
+/*
+ * hypic_conv_warmup -- the seam windows' inputs for models with a short
+ * causal depthwise convolution before the recurrence (codernav.top, linear
+ * layers, last paragraph: conv-state warm-up).  A seam window's first
+ * conv_k - 1 tokens take taps from the previous segment; this call feeds them
+ * the raw inputs just before the window:
+ *     y_t[c] = act( sum_{j<conv_k} taps[c][j] x_{t-conv_k+1+j}[c] )
+ * for t = d_tok_begin[i] .. + w - 1 (raw tokens before index 0 read as zero),
+ * for each of q, k, v.
+ *   raw        raw (pre-convolution) q, k, v, strided as hypic_tokens
+ *              (g, beta, gamma unused)
+ *   d_taps     [3][n_chains][dk][conv_k] fp32 (q, k, v), 1 <= conv_k <= 8
+ *   act        0: none, 1: SiLU  z / (1 + e^-z)
+ *   d_q_out, d_k_out, d_v_out  [n_items][w][n_chains][dk] in the input dtype,
+ *              ready to pass to hypic_compose / hypic_seam_advance as seam
+ *              tokens (tok_stride n_chains * dk, window i at token i * w).
+ */
+int hypic_conv_warmup(const hypic_layout *L, const hypic_tokens *raw, const float *d_taps, int32_t conv_k,
+                      int32_t act, int32_t n_items, const int64_t *d_tok_begin, int32_t w, void *d_q_out,
+                      void *d_k_out, void *d_v_out, void *stream);
 
 /* Static text for a status code. */
 const char *hypic_status_string(int status);

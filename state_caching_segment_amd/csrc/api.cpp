@@ -118,7 +118,7 @@ bool validate_on() {
 }
 
 // HYPIC_FAULT_INJECT: "1" or "all" fails every call that would launch, one of
-// "build", "compose", "seam" only that call, with HYPIC_E_DEVICE after its
+// "build", "compose", "seam", "rerotate", "conv" only that call, with HYPIC_E_DEVICE after its
 // arguments have been validated; nothing is enqueued.  A host-side stand-in
 // for a failed launch, so that callers can test their error paths without
 // making the GPU fail.
@@ -431,6 +431,82 @@ int hypic_compose_tree_noalloc(const hypic_layout *L, int32_t n_req, int32_t max
                                float *d_o, float *d_prefix_states, void *stream) {
     return compose_call(L, HYPIC_TREE, n_req, max_list_len, d_list_off, d_pair_id, n_slots, d_T, d_S, seam,
                         d_seam_begin, w, d_state, d_o, d_prefix_states, nullptr, 0, true, stream);
+}
+
+int hypic_rerotate(const hypic_layout *L, int32_t n_items, const int32_t *d_slot, const int64_t *d_offset,
+                   double rope_base, const float *d_T, const float *d_S, float *d_T_out, float *d_S_out,
+                   void *stream) {
+    int rc = check_layout(L);
+    if (rc) return rc;
+    if (n_items < 0) return fail(HYPIC_E_INVALID, "n_items < 0");
+    if (!(rope_base > 1.0)) return fail(HYPIC_E_INVALID, "rope_base must be above 1 (got %g)", rope_base);
+    if (L->family == HYPIC_GLA || L->family == HYPIC_KDA)
+        return fail(HYPIC_E_UNSUPPORTED,
+                    "re-rotation is exact only when the decay commutes with the rotation; per-channel gates do "
+                    "not (unless both channels of every pair decay alike)");
+    if (n_items == 0) return ok();
+    if (!d_slot || !d_offset || !d_T || !d_S || !d_T_out || !d_S_out) return fail(HYPIC_E_INVALID, "NULL pointer");
+    if (!aligned16(d_T) || !aligned16(d_S) || !aligned16(d_T_out) || !aligned16(d_S_out))
+        return fail(HYPIC_E_INVALID, "pairs must be 16-byte aligned");
+    if ((int64_t)n_items * L->n_chains > 0x7fffffff) return fail(HYPIC_E_INVALID, "n_items * n_chains too large");
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (validate_on()) {
+        std::vector<int32_t> sl;
+        if ((rc = read_back(sl, d_slot, n_items, st, "d_slot"))) return rc;
+        for (int i = 0; i < n_items; ++i)
+            if (sl[i] < 0) return fail(HYPIC_E_INVALID, "HYPIC_VALIDATE: item %d names slot %d", i, sl[i]);
+    }
+    if ((rc = injected("rerotate"))) return rc;
+    hy::RerotateArgs a{};
+    a.n_chains = L->n_chains;
+    a.dk = L->dk;
+    a.t_elems = hypic_t_elems(L->family, L->dk);
+    a.slot = d_slot;
+    a.offset = d_offset;
+    a.base = rope_base;
+    a.T = d_T;
+    a.S = d_S;
+    a.T_out = d_T_out;
+    a.S_out = d_S_out;
+    return launched(hy::rerotate(a, n_items, st), "re-rotation launch");
+}
+
+int hypic_conv_warmup(const hypic_layout *L, const hypic_tokens *raw, const float *d_taps, int32_t conv_k,
+                      int32_t act, int32_t n_items, const int64_t *d_tok_begin, int32_t w, void *d_q_out,
+                      void *d_k_out, void *d_v_out, void *stream) {
+    int rc = check_layout(L);
+    if (rc) return rc;
+    if (!raw || !raw->q || !raw->k || !raw->v) return fail(HYPIC_E_INVALID, "raw q, k and v are required");
+    if (raw->chain_stride < L->dk || raw->tok_stride < L->dk)
+        return fail(HYPIC_E_INVALID, "raw strides below dk");
+    if (conv_k < 1 || conv_k > 8) return fail(HYPIC_E_UNSUPPORTED, "conv_k must be 1 .. 8 (got %d)", conv_k);
+    if (act != 0 && act != 1) return fail(HYPIC_E_INVALID, "act must be 0 (none) or 1 (SiLU)");
+    if (n_items < 0 || w < 0) return fail(HYPIC_E_INVALID, "negative n_items or w");
+    if (n_items == 0 || w == 0) return ok();
+    if (!d_taps || !d_tok_begin || !d_q_out || !d_k_out || !d_v_out) return fail(HYPIC_E_INVALID, "NULL pointer");
+    if ((int64_t)n_items * L->n_chains > 0x7fffffff) return fail(HYPIC_E_INVALID, "n_items * n_chains too large");
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (validate_on()) {
+        std::vector<int64_t> tb;
+        if ((rc = read_back(tb, d_tok_begin, n_items, st, "d_tok_begin"))) return rc;
+        for (int i = 0; i < n_items; ++i)
+            if (tb[i] < 0)
+                return fail(HYPIC_E_INVALID, "HYPIC_VALIDATE: item %d starts at token %lld", i, (long long)tb[i]);
+    }
+    if ((rc = injected("conv"))) return rc;
+    hy::ConvArgs a{};
+    a.x = to_tok(raw);
+    a.n_chains = L->n_chains;
+    a.dk = L->dk;
+    a.w = w;
+    a.K = conv_k;
+    a.act = act;
+    a.tok_begin = d_tok_begin;
+    a.taps = d_taps;
+    a.q_out = d_q_out;
+    a.k_out = d_k_out;
+    a.v_out = d_v_out;
+    return launched(hy::conv_warmup(a, L->in_dtype == HYPIC_BF16, n_items, st), "conv warm-up launch");
 }
 
 int hypic_seam_advance(const hypic_layout *L, const hypic_tokens *x, int32_t n_items, const int64_t *d_tok_begin,

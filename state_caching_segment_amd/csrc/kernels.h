@@ -67,6 +67,36 @@ hipError_t compose_seq(const ComposeArgs &a, int family, bool bf16_in, int D, in
 hipError_t compose_tree(const TreeArgs &t, int family, bool bf16_in, int D, int n_req, hipStream_t st);
 hipError_t seam_advance(const SeamArgs &a, int family, bool bf16_in, int D, int n_items, hipStream_t st);
 
+// Re-rotation of cached pairs to absolute offsets (rotary embeddings): item i
+// reads slot slot[i] and writes (R T R^T, R S) at offset offset[i] to item i.
+struct RerotateArgs {
+    int n_chains;
+    int dk;
+    int64_t t_elems;      // 1 (scalar T) or dk * dk
+    const int32_t *slot;  // [item]
+    const int64_t *offset;
+    double base;
+    const float *T, *S;
+    float *T_out, *S_out;
+};
+
+// Conv warm-up of seam windows: q, k, v of tokens tok_begin[i] .. + w - 1
+// through the causal depthwise convolution, taps [3][chain][dk][K].
+struct ConvArgs {
+    Tok x;  // raw (pre-convolution) q, k, v
+    int n_chains;
+    int dk;
+    int w;
+    int K;
+    int act;  // 0: none, 1: SiLU
+    const int64_t *tok_begin;
+    const float *taps;
+    void *q_out, *k_out, *v_out;  // [item][w][chain][dk], input dtype
+};
+
+hipError_t rerotate(const RerotateArgs &a, int n_items, hipStream_t st);
+hipError_t conv_warmup(const ConvArgs &a, bool bf16_in, int n_items, hipStream_t st);
+
 // The library's own tree-compose workspace: kStaticWorkspaceBytes of device
 // memory per GPU (a file-scope device array), its address on the current
 // device in *ptr.  Every call on one GPU shares it.

@@ -1,0 +1,133 @@
+// Variant patches around the cached pair, for gfx950 (HYPIC, codernav.top
+// article, section on linear layers, last paragraph: conv-state warm-up and
+// state re-rotation).
+//
+// Re-rotation.  With rotary position embeddings on the keys, channel pairs
+// (i, i + d/2) are rotated by p * theta_i, theta_i = base^(-2i/d).  A pair
+// cached with its keys at local positions and reused at offset P becomes
+//     T' = R(P) T R(P)^T,   S' = R(P) S
+// (exact when the decay commutes with R(P): scalar gates, no gates).  R(P) is
+// block-diagonal in 2 x 2 rotations, so both are elementwise over quads of
+// rows (i, i + d/2) and columns (j, j + d/2): a pass bound by HBM.  Angles are
+// formed in fp64 and reduced modulo 2 pi before the fp32 rotation, so large
+// offsets lose nothing.
+//
+// Conv warm-up.  A short causal depthwise convolution (K taps) feeds the
+// recurrence; a seam window's first K - 1 tokens take taps from the previous
+// segment.  The kernel writes the window's convolved q, k, v with those taps
+// read from the raw inputs just before the window (tokens before index 0 read
+// as zero), optionally through SiLU.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace hy {
+
+constexpr int VAR_THREADS = 256;
+
+// One (item, chain) per workgroup.
+__global__ void __launch_bounds__(VAR_THREADS)
+k_rerotate(RerotateArgs a) {
+    __shared__ __attribute__((aligned(16))) float cs[64];
+    __shared__ __attribute__((aligned(16))) float sn[64];
+    const int item = blockIdx.x / a.n_chains, chain = blockIdx.x % a.n_chains;
+    const int dk = a.dk, h = dk / 2, tid = threadIdx.x;
+    if (tid < h) {
+        const double th = pow(a.base, -2.0 * tid / dk);
+        double ang = fmod((double)a.offset[item] * th, 6.283185307179586476925286766559);
+        float s, c;
+        sincosf((float)ang, &s, &c);
+        cs[tid] = c;
+        sn[tid] = s;
+    }
+    __syncthreads();
+    const int64_t slot = a.slot[item];
+    const float *T = a.T + (slot * a.n_chains + chain) * a.t_elems;
+    const float *S = a.S + (slot * a.n_chains + chain) * (int64_t)dk * dk;
+    float *To = a.T_out + ((int64_t)item * a.n_chains + chain) * a.t_elems;
+    float *So = a.S_out + ((int64_t)item * a.n_chains + chain) * (int64_t)dk * dk;
+    // S' = R S: row pairs (i, i + h), four columns per thread
+    const int q4 = dk / 4;
+    for (int it = tid; it < h * q4; it += VAR_THREADS) {
+        const int i = it / q4, j = 4 * (it % q4);
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(S + i * dk + j);
+        const f32x4 y = *reinterpret_cast<const f32x4 *>(S + (i + h) * dk + j);
+        const float c = cs[i], s = sn[i];
+        *reinterpret_cast<f32x4 *>(So + i * dk + j) = c * x - s * y;
+        *reinterpret_cast<f32x4 *>(So + (i + h) * dk + j) = s * x + c * y;
+    }
+    if (a.t_elems == 1) {
+        if (tid == 0) To[0] = T[0];  // a scalar transition commutes with R
+        return;
+    }
+    // T' = R T R^T: rows (i, i + h) x columns (j .. j+3, j+h .. j+h+3)
+    const int h4 = h / 4;  // (dk >= 16: h is a multiple of 4)
+    for (int it = tid; it < h * h4; it += VAR_THREADS) {
+        const int i = it / h4, j = 4 * (it % h4);
+        const f32x4 t00 = *reinterpret_cast<const f32x4 *>(T + i * dk + j);
+        const f32x4 t01 = *reinterpret_cast<const f32x4 *>(T + i * dk + j + h);
+        const f32x4 t10 = *reinterpret_cast<const f32x4 *>(T + (i + h) * dk + j);
+        const f32x4 t11 = *reinterpret_cast<const f32x4 *>(T + (i + h) * dk + j + h);
+        const float ci = cs[i], si = sn[i];
+        // rows
+        const f32x4 a00 = ci * t00 - si * t10, a01 = ci * t01 - si * t11;
+        const f32x4 a10 = si * t00 + ci * t10, a11 = si * t01 + ci * t11;
+        // columns
+        const f32x4 cj = *reinterpret_cast<const f32x4 *>(cs + j), sj = *reinterpret_cast<const f32x4 *>(sn + j);
+        *reinterpret_cast<f32x4 *>(To + i * dk + j) = cj * a00 - sj * a01;
+        *reinterpret_cast<f32x4 *>(To + i * dk + j + h) = sj * a00 + cj * a01;
+        *reinterpret_cast<f32x4 *>(To + (i + h) * dk + j) = cj * a10 - sj * a11;
+        *reinterpret_cast<f32x4 *>(To + (i + h) * dk + j + h) = sj * a10 + cj * a11;
+    }
+}
+
+template <typename TIN>
+__global__ void __launch_bounds__(VAR_THREADS)
+k_conv_warmup(ConvArgs a) {
+    constexpr int KMAX = 8;
+    const int item = blockIdx.x / a.n_chains, chain = blockIdx.x % a.n_chains;
+    const int64_t s0 = a.tok_begin[item];
+    for (int it = threadIdx.x; it < 3 * a.dk; it += VAR_THREADS) {
+        const int which = it / a.dk, c = it % a.dk;  // 0: q, 1: k, 2: v
+        const TIN *x = reinterpret_cast<const TIN *>(which == 0 ? a.x.q : which == 1 ? a.x.k : a.x.v) +
+                       (int64_t)chain * a.x.cs + c;
+        TIN *y = reinterpret_cast<TIN *>(which == 0 ? a.q_out : which == 1 ? a.k_out : a.v_out) +
+                 ((int64_t)item * a.w * a.n_chains + chain) * a.dk + c;
+        const float *tp = a.taps + (((int64_t)which * a.n_chains + chain) * a.dk + c) * a.K;
+        float taps[KMAX], win[KMAX];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            taps[j] = j < a.K ? tp[j] : 0.f;
+            // window slot j holds token s0 - K + 1 + j (history first)
+            const int64_t u = s0 - a.K + 1 + j;
+            win[j] = (j < a.K - 1 && u >= 0) ? (float)x[u * a.x.ts] : 0.f;
+        }
+        for (int t = 0; t < a.w; ++t) {
+            win[a.K - 1 < KMAX ? a.K - 1 : KMAX - 1] = (float)x[(s0 + t) * a.x.ts];
+            float z = 0.f;
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j) z += j < a.K ? taps[j] * win[j] : 0.f;
+            if (a.act == 1) z = z / (1.f + __expf(-z));
+            y[(int64_t)t * a.n_chains * a.dk] = (TIN)z;
+#pragma unroll
+            for (int j = 0; j + 1 < KMAX; ++j) win[j] = win[j + 1];
+        }
+    }
+}
+
+hipError_t rerotate(const RerotateArgs &a, int n_items, hipStream_t st) {
+    hipLaunchKernelGGL(k_rerotate, dim3((unsigned)((int64_t)n_items * a.n_chains)), dim3(VAR_THREADS), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t conv_warmup(const ConvArgs &a, bool bf16_in, int n_items, hipStream_t st) {
+    const dim3 grid((unsigned)((int64_t)n_items * a.n_chains)), block(VAR_THREADS);
+    if (bf16_in)
+        hipLaunchKernelGGL(k_conv_warmup<bf16>, grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL(k_conv_warmup<float>, grid, block, 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace hy

@@ -25,7 +25,8 @@ OP_BUILD, OP_COMPOSE_SEQ, OP_COMPOSE_TREE, OP_SEAM = 0, 1, 2, 3
 STATUS = {0: "HYPIC_OK", -1: "HYPIC_E_INVALID", -2: "HYPIC_E_UNSUPPORTED", -3: "HYPIC_E_WORKSPACE",
           -4: "HYPIC_E_DEVICE"}
 EXPORTS = ("hypic_t_elems", "hypic_workspace_bytes", "hypic_segment_build", "hypic_segment_prefill",
-           "hypic_compose", "hypic_compose_tree_noalloc", "hypic_seam_advance", "hypic_status_string", "hypic_last_error")
+           "hypic_compose", "hypic_compose_tree_noalloc", "hypic_seam_advance", "hypic_rerotate",
+           "hypic_conv_warmup", "hypic_status_string", "hypic_last_error")
 NOALLOC_WORKSPACE_BYTES = 64 << 20  # HYPIC_NOALLOC_WORKSPACE_BYTES
 
 
@@ -76,6 +77,10 @@ def load(path: str = LIB_PATH, cache: bool = True) -> ctypes.CDLL:
     lib.hypic_compose_tree_noalloc.restype = ctypes.c_int
     lib.hypic_seam_advance.argtypes = [P, P, i32, P, i32, P, P, P]
     lib.hypic_seam_advance.restype = ctypes.c_int
+    lib.hypic_rerotate.argtypes = [P, i32, P, P, ctypes.c_double, P, P, P, P, P]
+    lib.hypic_rerotate.restype = ctypes.c_int
+    lib.hypic_conv_warmup.argtypes = [P, P, P, i32, i32, i32, P, i32, P, P, P, P]
+    lib.hypic_conv_warmup.restype = ctypes.c_int
     lib.hypic_status_string.argtypes = [ctypes.c_int]
     lib.hypic_status_string.restype = ctypes.c_char_p
     lib.hypic_last_error.argtypes = []
@@ -175,6 +180,18 @@ def hypic_seam_advance(L: hypic_layout, x: hypic_tokens, n_items: int, tok_begin
                        stream=None) -> None:
     _check(load().hypic_seam_advance(ctypes.byref(L), ctypes.byref(x), n_items, _p(tok_begin), w, _p(state), _p(o),
                                      _stream(stream)))
+
+
+def hypic_rerotate(L: hypic_layout, n_items: int, slot, offset, rope_base: float, T, S, T_out, S_out,
+                   stream=None) -> None:
+    _check(load().hypic_rerotate(ctypes.byref(L), n_items, _p(slot), _p(offset), float(rope_base), _p(T), _p(S),
+                                 _p(T_out), _p(S_out), _stream(stream)))
+
+
+def hypic_conv_warmup(L: hypic_layout, raw: hypic_tokens, taps, conv_k: int, act: int, n_items: int, tok_begin,
+                      w: int, q_out, k_out, v_out, stream=None) -> None:
+    _check(load().hypic_conv_warmup(ctypes.byref(L), ctypes.byref(raw), _p(taps), conv_k, act, n_items,
+                                    _p(tok_begin), w, _p(q_out), _p(k_out), _p(v_out), _stream(stream)))
 
 
 def hypic_status_string(status: int) -> str:

@@ -223,3 +223,35 @@ def test_request_plan_longest_first():
     assert (q.list_off == p.list_off).all() and (q.seam_begin == p.seam_begin).all()
     with pytest.raises(ValueError):
         request_plan(reqs, 8, slot_order="random")
+
+
+def test_variant_calls_validation():
+    """hypic_rerotate and hypic_conv_warmup reject bad arguments before any
+    HIP call; families whose per-channel decay does not commute with the
+    rotation are refused."""
+    rr = hy.hypic_rerotate
+    L = hy.layout("gdn", "f32", 4, 64)
+    expect(-2, rr, hy.layout("gla", "bf16", 4, 64), 1, 8, 8, 10000.0, 16, 16, 16, 16)
+    expect(-2, rr, hy.layout("kda", "bf16", 4, 64), 1, 8, 8, 10000.0, 16, 16, 16, 16)
+    expect(-1, rr, L, 1, 8, 8, 1.0, 16, 16, 16, 16)           # base not above 1
+    expect(-1, rr, L, -1, 8, 8, 10000.0, 16, 16, 16, 16)      # n_items < 0
+    expect(-1, rr, L, 1, None, 8, 10000.0, 16, 16, 16, 16)    # NULL slot
+    expect(-1, rr, L, 1, 8, 8, 10000.0, 16, 16, 18, 16)       # misaligned output
+    rr(L, 0, None, None, 10000.0, None, None, None, None)     # nothing to do
+    cw = hy.hypic_conv_warmup
+    x = _fake_tokens("gdn", "f32", cs=64)
+    expect(-2, cw, L, x, 16, 9, 1, 1, 8, 8, 16, 16, 16)       # conv_k > 8
+    expect(-2, cw, L, x, 16, 0, 1, 1, 8, 8, 16, 16, 16)       # conv_k < 1
+    expect(-1, cw, L, x, 16, 4, 2, 1, 8, 8, 16, 16, 16)       # act
+    expect(-1, cw, L, x, None, 4, 1, 1, 8, 8, 16, 16, 16)     # NULL taps
+    xq = _fake_tokens("gdn", "f32", cs=64)
+    xq.q = None
+    expect(-1, cw, L, xq, 16, 4, 1, 1, 8, 8, 16, 16, 16)      # raw q required
+    cw(L, x, None, 4, 1, 0, None, 8, None, None, None)        # nothing to do
+    os.environ["HYPIC_FAULT_INJECT"] = "rerotate"
+    try:
+        expect(-4, rr, L, 1, 8, 8, 10000.0, 16, 16, 16, 16)
+        os.environ["HYPIC_FAULT_INJECT"] = "conv"
+        expect(-4, cw, L, x, 16, 4, 1, 1, 8, 8, 16, 16, 16)
+    finally:
+        del os.environ["HYPIC_FAULT_INJECT"]
