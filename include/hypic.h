@@ -287,6 +287,37 @@ int hypic_conv_warmup(const hypic_layout *L, const hypic_tokens *raw, const floa
                       int32_t act, int32_t n_items, const int64_t *d_tok_begin, int32_t w, void *d_q_out,
                       void *d_k_out, void *d_v_out, void *stream);
 
+/*
+ * Pair store -- the host-side index of a pool of cached pairs (codernav.top,
+ * segment parallelism: the router probes which segments hit the cache;
+ * misses are inevitable as the corpus changes and rarely used documents are
+ * evicted).  The pool is device memory the caller owns: slots
+ * 0 .. n_slots-1 of the T and S arrays that hypic_segment_build writes and
+ * hypic_compose reads.  The store maps a segment's content key (for example
+ * hypic_content_key of its token ids) to its slot; it allocates host memory
+ * only and is not thread-safe (one caller at a time per store).
+ *
+ * hypic_store_acquire gives every one of n keys a slot: a key already in the
+ * store keeps its slot (a hit); a new key (a miss, miss_out = 1: the caller
+ * builds its pair into that slot before composing) takes a free slot, else
+ * evicts the entry acquired least often, ties broken by least recent
+ * acquisition, never one named earlier in the same call.  Free slots are
+ * handed out lowest first, then most recently freed first.  Returns the
+ * number of misses, HYPIC_E_WORKSPACE (and changes nothing) if the call names
+ * more distinct keys than the pool has slots, or HYPIC_E_INVALID.
+ * hypic_store_evict drops a key (returns 1 if it was present, else 0);
+ * hypic_store_stats fills out[4] = {entries, hits, misses, evictions}.
+ */
+typedef struct hypic_store hypic_store;
+hypic_store *hypic_store_create(int64_t n_slots); /* NULL if n_slots is not in 1 .. 2^31-1 */
+void hypic_store_destroy(hypic_store *store);
+int hypic_store_acquire(hypic_store *store, int32_t n, const uint64_t *keys, int32_t *slots_out,
+                        uint8_t *miss_out);
+int hypic_store_evict(hypic_store *store, uint64_t key);
+int hypic_store_stats(const hypic_store *store, int64_t *out);
+/* 64-bit FNV-1a hash of nbytes of host memory: a content key. */
+uint64_t hypic_content_key(const void *data, size_t nbytes);
+
 /* Static text for a status code. */
 const char *hypic_status_string(int status);
 /* Detail of the last failing call on this thread ("" if none). */

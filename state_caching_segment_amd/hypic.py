@@ -26,7 +26,8 @@ STATUS = {0: "HYPIC_OK", -1: "HYPIC_E_INVALID", -2: "HYPIC_E_UNSUPPORTED", -3: "
           -4: "HYPIC_E_DEVICE"}
 EXPORTS = ("hypic_t_elems", "hypic_workspace_bytes", "hypic_segment_build", "hypic_segment_prefill",
            "hypic_compose", "hypic_compose_tree_noalloc", "hypic_seam_advance", "hypic_rerotate",
-           "hypic_conv_warmup", "hypic_status_string", "hypic_last_error")
+           "hypic_conv_warmup", "hypic_store_create", "hypic_store_destroy", "hypic_store_acquire",
+           "hypic_store_evict", "hypic_store_stats", "hypic_content_key", "hypic_status_string", "hypic_last_error")
 NOALLOC_WORKSPACE_BYTES = 64 << 20  # HYPIC_NOALLOC_WORKSPACE_BYTES
 
 
@@ -81,6 +82,18 @@ def load(path: str = LIB_PATH, cache: bool = True) -> ctypes.CDLL:
     lib.hypic_rerotate.restype = ctypes.c_int
     lib.hypic_conv_warmup.argtypes = [P, P, P, i32, i32, i32, P, i32, P, P, P, P]
     lib.hypic_conv_warmup.restype = ctypes.c_int
+    lib.hypic_store_create.argtypes = [i64]
+    lib.hypic_store_create.restype = P
+    lib.hypic_store_destroy.argtypes = [P]
+    lib.hypic_store_destroy.restype = None
+    lib.hypic_store_acquire.argtypes = [P, i32, P, P, P]
+    lib.hypic_store_acquire.restype = ctypes.c_int
+    lib.hypic_store_evict.argtypes = [P, ctypes.c_uint64]
+    lib.hypic_store_evict.restype = ctypes.c_int
+    lib.hypic_store_stats.argtypes = [P, P]
+    lib.hypic_store_stats.restype = ctypes.c_int
+    lib.hypic_content_key.argtypes = [P, sz]
+    lib.hypic_content_key.restype = ctypes.c_uint64
     lib.hypic_status_string.argtypes = [ctypes.c_int]
     lib.hypic_status_string.restype = ctypes.c_char_p
     lib.hypic_last_error.argtypes = []
@@ -192,6 +205,57 @@ def hypic_conv_warmup(L: hypic_layout, raw: hypic_tokens, taps, conv_k: int, act
                       w: int, q_out, k_out, v_out, stream=None) -> None:
     _check(load().hypic_conv_warmup(ctypes.byref(L), ctypes.byref(raw), _p(taps), conv_k, act, n_items,
                                     _p(tok_begin), w, _p(q_out), _p(k_out), _p(v_out), _stream(stream)))
+
+
+class Store:
+    """A pair store (hypic_store_*): content keys to slots of a caller-owned
+    pool of pairs."""
+
+    def __init__(self, n_slots: int):
+        self._lib = load()
+        self.h = self._lib.hypic_store_create(int(n_slots))
+        if not self.h:
+            raise HypicError(-1, f"cannot create a store of {n_slots} slots")
+        self.n_slots = int(n_slots)
+
+    def acquire(self, keys):
+        """-> (slots int32 array, miss bool array); raises HypicError."""
+        import numpy as np
+        k = np.ascontiguousarray(np.asarray(keys, dtype=np.uint64))
+        slots = np.empty(len(k), np.int32)
+        miss = np.empty(len(k), np.uint8)
+        rc = self._lib.hypic_store_acquire(self.h, len(k), k.ctypes.data, slots.ctypes.data, miss.ctypes.data)
+        if rc < 0:
+            raise HypicError(rc, "store acquire refused (more distinct keys than slots)" if rc == -3 else "bad store call")
+        return slots, miss.astype(bool)
+
+    def evict(self, key) -> bool:
+        return self._lib.hypic_store_evict(self.h, int(key)) == 1
+
+    def stats(self):
+        import numpy as np
+        out = np.zeros(4, np.int64)
+        _check(self._lib.hypic_store_stats(self.h, out.ctypes.data))
+        return dict(zip(("entries", "hits", "misses", "evictions"), (int(x) for x in out)))
+
+    def close(self):
+        if self.h:
+            self._lib.hypic_store_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def hypic_content_key(data) -> int:
+    """FNV-1a 64 of a bytes-like object or a numpy array's bytes."""
+    import numpy as np
+    b = np.ascontiguousarray(data).tobytes() if not isinstance(data, (bytes, bytearray)) else bytes(data)
+    buf = ctypes.create_string_buffer(b, len(b))
+    return int(load().hypic_content_key(buf, len(b)))
 
 
 def hypic_status_string(status: int) -> str:
