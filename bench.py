@@ -538,6 +538,21 @@ def main():
                           "tokens_per_s": v_tokens / tp, "ms_over_build": tp / tb, "roofline": rp}
         del pout, pT, pS
         torch.cuda.empty_cache()
+    # compact pairs (bf16 T^ with a power-of-two scale): the same compose over them
+    if wl.family in ("deltanet", "gdn") and wl.dtype == "bf16" and d >= 64 and not tree:
+        Tc = torch.empty(plan.n_slots, C, d * d, dtype=torch.bfloat16, device="cuda")
+        sc = torch.empty(plan.n_slots, C, device="cuda")
+        hy.hypic_pair_compact(lay.L, plan.n_slots, lay.T, Tc, sc, stream=stream)
+
+        def cc():
+            lay.state.zero_()
+            hy.hypic_compose_compact(lay.L, plan.n_req, plan.max_list_len, lay.lo, lay.pid, plan.n_slots, Tc, sc,
+                                     lay.S, lay.x, lay.seam, w, lay.state, lay.o, stream=stream)
+        ms = _median_ms(cc, args.steps, stream) - _median_ms(lambda: lay.state.zero_(), args.steps, stream)
+        cbc = cb - len(plan.pair_id) * C * d * d * 2.0   # T read in bf16: half its fp32 bytes
+        out["compose_compact"] = {"ms": ms, "roofline": roof(cbc, cf, ms * 1e-3, "hbm") |
+                                  {"kernel": "k_compose_lean (compact pairs)", "traffic": None}}
+        del Tc, sc
     # variant patches at this shape: every cached pair re-rotated to its body's
     # absolute offset (rotary embeddings), and the seam windows' convolved
     # q, k, v from raw inputs (short convolution, 4 taps, SiLU)

@@ -60,7 +60,7 @@
  *     only.  The detail of the last error on the calling thread is in
  *     hypic_last_error().  On error the outputs are unspecified.
  *   - HYPIC_FAULT_INJECT ("1" or "all"; or "build", "compose", "seam",
- *     "rerotate", "conv" for one call): after its arguments have been validated, the call returns
+ *     "rerotate", "conv", "compact" for one call): after its arguments have been validated, the call returns
  *     HYPIC_E_DEVICE and enqueues nothing.  For testing callers' error paths.
  *   - dv must equal dk (HYPIC_E_UNSUPPORTED otherwise): every kernel keeps the
  *     state and T in tiles of the same width, and every workload these
@@ -286,6 +286,28 @@ int hypic_rerotate(const hypic_layout *L, int32_t n_items, const int32_t *d_slot
 int hypic_conv_warmup(const hypic_layout *L, const hypic_tokens *raw, const float *d_taps, int32_t conv_k,
                       int32_t act, int32_t n_items, const int64_t *d_tok_begin, int32_t w, void *d_q_out,
                       void *d_k_out, void *d_v_out, void *stream);
+
+/*
+ * Compact pairs (precision of the pair store; codernav.top, summary: tiered
+ * caching of the pairs).  hypic_pair_compact converts the dense T of n_slots
+ * slots to bf16 T^ with a power-of-two scale per (slot, chain):
+ *     T = sigma T^,   sigma = 2^e where max|T| = m 2^e, m in [0.5, 1)
+ * (|T^| < 1, the scaling exact; T = 0 keeps sigma = 1).  For GDN sigma
+ * absorbs the segment's total decay.  Outputs d_Tc [n_slots][n_chains][dk][dk]
+ * bf16 (8-byte aligned), d_Tscale [n_slots][n_chains] fp32; S is unchanged.
+ * Dense families only.  hypic_compose_compact is the sequential
+ * hypic_compose over compact pairs (T^ read in bf16: 64 + 32 KiB per pair and
+ * chain at d = 128 instead of 128 KiB); DeltaNet and GDN with bf16 inputs,
+ * dk >= 64.  T^'s rounding (relative 2^-8 at most per element) enters each step's
+ * T S, so its error is that of bf16 T, not of the fp32 pair.
+ */
+int hypic_pair_compact(const hypic_layout *L, int32_t n_slots, const float *d_T, void *d_Tc, float *d_Tscale,
+                       void *stream);
+int hypic_compose_compact(const hypic_layout *L, int32_t n_req, int32_t max_list_len,
+                          const int32_t *d_list_off, const int32_t *d_pair_id, int64_t n_slots,
+                          const void *d_Tc, const float *d_Tscale, const float *d_S,
+                          const hypic_tokens *seam, const int64_t *d_seam_begin, int32_t w,
+                          float *d_state, float *d_o, float *d_prefix_states, void *stream);
 
 /*
  * Pair store -- the host-side index of a pool of cached pairs (codernav.top,

@@ -175,8 +175,12 @@ def request_batch(family: str, bounds, w: int, q, k, v, g=None, beta=None, gamma
 
 
 def rel_fro(x, ref) -> float:
-    """Relative Frobenius error ||x - ref||_F / ||ref||_F (inf-safe for ref = 0)."""
+    """Relative Frobenius error ||x - ref||_F / ||ref||_F (inf-safe for ref = 0);
+    infinite when x is not finite, so that a maximum over objects cannot pass
+    over a NaN."""
     x, ref = np.asarray(x, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    if not np.isfinite(x).all():
+        return float("inf")
     nr = np.linalg.norm(ref)
     d = np.linalg.norm(x - ref)
     return float(d / nr) if nr > 0 else float(d)

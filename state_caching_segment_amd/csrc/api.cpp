@@ -118,7 +118,7 @@ bool validate_on() {
 }
 
 // HYPIC_FAULT_INJECT: "1" or "all" fails every call that would launch, one of
-// "build", "compose", "seam", "rerotate", "conv" only that call, with HYPIC_E_DEVICE after its
+// "build", "compose", "seam", "rerotate", "conv", "compact" only that call, with HYPIC_E_DEVICE after its
 // arguments have been validated; nothing is enqueued.  A host-side stand-in
 // for a failed launch, so that callers can test their error paths without
 // making the GPU fail.
@@ -325,7 +325,7 @@ int compose_call(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t max
         if ((rc = check_tokens(L, seam, true))) return rc;
         if (!d_seam_begin || !d_o) return fail(HYPIC_E_INVALID, "seams need d_seam_begin and d_o");
     }
-    hy::ComposeArgs a;
+    hy::ComposeArgs a{};
     a.x = has_seam ? to_tok(seam) : hy::Tok{};
     a.n_chains = L->n_chains;
     a.dk = L->dk;
@@ -431,6 +431,66 @@ int hypic_compose_tree_noalloc(const hypic_layout *L, int32_t n_req, int32_t max
                                float *d_o, float *d_prefix_states, void *stream) {
     return compose_call(L, HYPIC_TREE, n_req, max_list_len, d_list_off, d_pair_id, n_slots, d_T, d_S, seam,
                         d_seam_begin, w, d_state, d_o, d_prefix_states, nullptr, 0, true, stream);
+}
+
+int hypic_pair_compact(const hypic_layout *L, int32_t n_slots, const float *d_T, void *d_Tc, float *d_Tscale,
+                       void *stream) {
+    int rc = check_layout(L);
+    if (rc) return rc;
+    if (!dense(L->family)) return fail(HYPIC_E_UNSUPPORTED, "compact pairs are for dense transitions");
+    if (n_slots < 0) return fail(HYPIC_E_INVALID, "n_slots < 0");
+    if (n_slots == 0) return ok();
+    if (!d_T || !d_Tc || !d_Tscale) return fail(HYPIC_E_INVALID, "NULL pointer");
+    if (!aligned16(d_T) || (reinterpret_cast<uintptr_t>(d_Tc) & 7))
+        return fail(HYPIC_E_INVALID, "T must be 16-byte and the compact T 8-byte aligned");
+    if ((int64_t)n_slots * L->n_chains > 0x7fffffff) return fail(HYPIC_E_INVALID, "n_slots * n_chains too large");
+    if ((rc = injected("compact"))) return rc;
+    return launched(hy::pair_compact(d_T, static_cast<hy::bf16 *>(d_Tc), d_Tscale, L->dk, (int64_t)n_slots * L->n_chains,
+                                     reinterpret_cast<hipStream_t>(stream)),
+                    "pair compaction launch");
+}
+
+int hypic_compose_compact(const hypic_layout *L, int32_t n_req, int32_t max_list_len, const int32_t *d_list_off,
+                          const int32_t *d_pair_id, int64_t n_slots, const void *d_Tc, const float *d_Tscale,
+                          const float *d_S, const hypic_tokens *seam, const int64_t *d_seam_begin, int32_t w,
+                          float *d_state, float *d_o, float *d_prefix_states, void *stream) {
+    int rc = check_layout(L);
+    if (rc) return rc;
+    if (!(L->family == HYPIC_DELTANET || L->family == HYPIC_GDN) || L->in_dtype != HYPIC_BF16 || L->dk < 64)
+        return fail(HYPIC_E_UNSUPPORTED, "compact-pair compose is implemented for DeltaNet and GDN, bf16, dk >= 64");
+    if (n_req < 0 || max_list_len < 0 || n_slots < 0 || w < 0) return fail(HYPIC_E_INVALID, "negative size");
+    if (n_req == 0) return ok();
+    if (!d_list_off || !d_state) return fail(HYPIC_E_INVALID, "NULL list or state pointer");
+    if (max_list_len > 0 && (!d_pair_id || !d_Tc || !d_Tscale || !d_S))
+        return fail(HYPIC_E_INVALID, "NULL pair pointer");
+    if ((int64_t)n_req * L->n_chains > 0x7fffffff) return fail(HYPIC_E_INVALID, "n_req * n_chains too large");
+    const bool has_seam = seam != nullptr && w > 0;
+    if (has_seam) {
+        if ((rc = check_tokens(L, seam, true))) return rc;
+        if (!d_seam_begin || !d_o) return fail(HYPIC_E_INVALID, "seams need d_seam_begin and d_o");
+    }
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (validate_on() &&
+        (rc = validate_lists(n_req, max_list_len, d_list_off, d_pair_id, n_slots, has_seam ? d_seam_begin : nullptr, st)))
+        return rc;
+    if ((rc = injected("compose"))) return rc;
+    hy::ComposeArgs a{};
+    a.x = has_seam ? to_tok(seam) : hy::Tok{};
+    a.n_chains = L->n_chains;
+    a.dk = L->dk;
+    a.w = has_seam ? w : 0;
+    a.has_seam = has_seam ? 1 : 0;
+    a.list_off = d_list_off;
+    a.pair_id = d_pair_id;
+    a.T = static_cast<const float *>(d_Tc);
+    a.t_scale = d_Tscale;
+    a.S = d_S;
+    a.t_elems = (int64_t)L->dk * L->dk;
+    a.seam_begin = d_seam_begin;
+    a.state = d_state;
+    a.o = d_o;
+    a.prefix = d_prefix_states;
+    return launched(hy::compose_seq_compact(a, L->family, L->dk, n_req, st), "compact compose launch");
 }
 
 int hypic_rerotate(const hypic_layout *L, int32_t n_items, const int32_t *d_slot, const int64_t *d_offset,

@@ -473,7 +473,11 @@ k_compose_dense(TreeArgs t) {
 // product.
 // PREFIX: also store the state after every entry to a.prefix (a separate
 // instantiation, so that the plain form carries no trace of it).
-template <int D, int FAM, bool SCAN = false, bool PREFIX = false>
+// TC: compact pairs: T is stored as bf16 T^ with a power-of-two scale per
+// (slot, chain), T = sigma T^ (a.T points at the bf16 values, a.t_scale at
+// the scales).  T^ is staged as it stands (no split) and the product takes
+// two passes, T^ S_hi + T^ S_lo; the scale joins the add of S_j.
+template <int D, int FAM, bool SCAN = false, bool PREFIX = false, bool TC = false>
 __global__ void __launch_bounds__(D / 32 * 64, 2)
 k_compose_lean(TreeArgs targ) {
     static_assert(D >= 64 && (FAM == DELTANET || FAM == GDN), "lean compose: d >= 64, scalar-gate erasing families");
@@ -481,8 +485,8 @@ k_compose_lean(TreeArgs targ) {
     constexpr int NW = D / 32, RT = D / 16, KB = D / 32;
     using TL = DenseTLds<D, false>;
     constexpr int LDT = TL::LDT;
-    constexpr int NV = D * D / 4 / 64 / NW;  // 16-byte pieces of T per lane
-    constexpr int RPW = D / NW;              // T rows staged by one wave
+    constexpr int NV = D * D / (TC ? 8 : 4) / 64 / NW;  // 16-byte pieces of T per lane
+    constexpr int RPW = D / NW;                         // T rows staged by one wave
     constexpr int dk = D;
     __shared__ __attribute__((aligned(16))) bf16 tsm[D * LDT];
     __shared__ SeamSmemB<D> sm;
@@ -518,9 +522,18 @@ k_compose_lean(TreeArgs targ) {
     // offset, the rest compile-time immediates (no per-load address math).
     // T: lane ln of wave wv stages rows wv*RPW + i*(256/D) + ln/(D/4), columns
     // 4 (ln % (D/4)) .. +3, for i < NV.
-    constexpr int TROWS = 256 / D;  // rows of T per 64-lane piece
-    f32x4 tpre[NV];
+    constexpr int TROWS = (TC ? 512 : 256) / D;  // rows of T per 64-lane piece
+    f32x4 tpre[NV];  // (TC: eight bf16 as raw bits)
     auto t_load = [&](int j, int ln) {
+        if constexpr (TC) {
+            const auto r = buffer_view(reinterpret_cast<const bf16 *>(a.T) + (pid_at(j) * a.n_chains + chain) * D * D,
+                                       D * D * 2);
+            const int voff = ((wv * RPW + (int)((unsigned)ln / (D / 8))) * D + 8 * (int)((unsigned)ln % (D / 8))) * 2;
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                tpre[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, i * TROWS * D * 2, 0));
+            return;
+        }
         const auto r = buffer_view(a.T + (pid_at(j) * a.n_chains + chain) * a.t_elems, D * D * 4);
         const int voff = ((wv * RPW + (int)((unsigned)ln / (D / 4))) * D + 4 * (int)((unsigned)ln % (D / 4))) * 4;
 #pragma unroll
@@ -528,6 +541,20 @@ k_compose_lean(TreeArgs targ) {
             tpre[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, i * TROWS * D * 4, 0));
     };
     auto t_put = [&](int ln) {
+        if constexpr (TC) {
+            // columns 8 c8 .. 8 c8 + 7 are the 4-column groups 2 c8 and 2 c8 + 1,
+            // placed as the fp32 path places them (hi half of the row only)
+            const int c8 = (int)((unsigned)ln % (D / 8));
+            auto pos = [](int c4) { const int sub = c4 % 8; return 32 * (c4 / 8) + 8 * (sub % 4) + 4 * (sub / 4); };
+            bf16 *tr = tsm + (wv * RPW + (int)((unsigned)ln / (D / 8))) * LDT;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const u32x4 u = __builtin_bit_cast(u32x4, tpre[i]);
+                *reinterpret_cast<u32x2 *>(tr + i * TROWS * LDT + pos(2 * c8)) = u32x2{u[0], u[1]};
+                *reinterpret_cast<u32x2 *>(tr + i * TROWS * LDT + pos(2 * c8 + 1)) = u32x2{u[2], u[3]};
+            }
+            return;
+        }
         // columns permuted within each 32-block so that a lane's A fragment
         // (k = 4grp.., 16+4grp..) is 8 consecutive bf16
         const int c4 = (int)((unsigned)ln % (D / 4)), sub = c4 % 8;
@@ -629,6 +656,7 @@ k_compose_lean(TreeArgs targ) {
                 split8(xv, xh[kb][nt], xl[kb][nt]);
             }
         s_load(j, ln);
+        const float sig = TC ? a.t_scale[pid_at(j) * a.n_chains + chain] : 1.f;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -642,12 +670,20 @@ k_compose_lean(TreeArgs targ) {
             for (int kb = 0; kb < KB; ++kb) {
                 const int off = (16 * rt + lr16) * LDT + 32 * kb + 8 * lgrp;
                 const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(tsm + off);
-                const bf16x8 al = *reinterpret_cast<const bf16x8 *>(tsm + D + off);
+                if constexpr (TC) {
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    X[rt][nt] = mfma(ah, xh[kb][nt], X[rt][nt]);
-                    X[rt][nt] = mfma(ah, xl[kb][nt], X[rt][nt]);
-                    X[rt][nt] = mfma(al, xh[kb][nt], X[rt][nt]);
+                    for (int nt = 0; nt < 2; ++nt) {
+                        X[rt][nt] = mfma(ah, xh[kb][nt], X[rt][nt]);
+                        X[rt][nt] = mfma(ah, xl[kb][nt], X[rt][nt]);
+                    }
+                } else {
+                    const bf16x8 al = *reinterpret_cast<const bf16x8 *>(tsm + D + off);
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        X[rt][nt] = mfma(ah, xh[kb][nt], X[rt][nt]);
+                        X[rt][nt] = mfma(ah, xl[kb][nt], X[rt][nt]);
+                        X[rt][nt] = mfma(al, xh[kb][nt], X[rt][nt]);
+                    }
                 }
             }
 #pragma unroll
@@ -655,7 +691,12 @@ k_compose_lean(TreeArgs targ) {
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) X[rt][nt][jj] += spre[rt][nt][jj];
+                for (int jj = 0; jj < 4; ++jj) {
+                    if constexpr (TC)
+                        X[rt][nt][jj] = sig * X[rt][nt][jj] + spre[rt][nt][jj];
+                    else
+                        X[rt][nt][jj] += spre[rt][nt][jj];
+                }
         if constexpr (PREFIX && !SCAN) {
             // the state after entry e
             const auto r = buffer_view(a.prefix + ((int64_t)e * a.n_chains + chain) * dk * dk, D * D * 4);
@@ -1037,6 +1078,24 @@ static hipError_t launch_compose(const ComposeArgs &a, int n_req, hipStream_t st
     } else
         hipLaunchKernelGGL((k_compose_seq<D, FAM, TIN>), grid, block, 0, st, a);
     return hipGetLastError();
+}
+
+hipError_t compose_seq_compact(const ComposeArgs &a, int family, int D, int n_req, hipStream_t st) {
+    const dim3 grid((unsigned)(n_req * (int64_t)a.n_chains)), block(D / 32 * 64);
+    TreeArgs t{};
+    t.c = a;
+#define HY_COMPACT(DD, FF)                                                                                   \
+    if (a.prefix)                                                                                          \
+        hipLaunchKernelGGL((k_compose_lean<DD, FF, false, true, true>), grid, block, 0, st, t);            \
+    else                                                                                                   \
+        hipLaunchKernelGGL((k_compose_lean<DD, FF, false, false, true>), grid, block, 0, st, t);           \
+    return hipGetLastError();
+    if (D == 128 && family == GDN) { HY_COMPACT(128, GDN) }
+    if (D == 128 && family == DELTANET) { HY_COMPACT(128, DELTANET) }
+    if (D == 64 && family == GDN) { HY_COMPACT(64, GDN) }
+    if (D == 64 && family == DELTANET) { HY_COMPACT(64, DELTANET) }
+#undef HY_COMPACT
+    return hipErrorInvalidValue;
 }
 
 template <int D, int FAM, typename TIN>

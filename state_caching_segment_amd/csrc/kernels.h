@@ -34,6 +34,7 @@ struct ComposeArgs {
     float *state;   // [req][chain][dk][dk]
     float *o;       // [entry][w][chain][dk]
     float *prefix;  // [entry][chain][dk][dk]: state after each entry, or null
+    const float *t_scale;  // compact pairs: T = t_scale[slot][chain] * T^ (bf16 at T); else null
 };
 
 struct SeamArgs {
@@ -66,6 +67,10 @@ hipError_t build_diag(const BuildArgs &a, int family, bool bf16_in, int D, int n
 hipError_t compose_seq(const ComposeArgs &a, int family, bool bf16_in, int D, int n_req, hipStream_t st);
 hipError_t compose_tree(const TreeArgs &t, int family, bool bf16_in, int D, int n_req, hipStream_t st);
 hipError_t seam_advance(const SeamArgs &a, int family, bool bf16_in, int D, int n_items, hipStream_t st);
+// sequential compose of compact pairs (DeltaNet, GDN; bf16 inputs; D 64 or 128)
+hipError_t compose_seq_compact(const ComposeArgs &a, int family, int D, int n_req, hipStream_t st);
+// compact pairs: T^ (bf16) and the power-of-two scale of each (slot, chain) from fp32 T
+hipError_t pair_compact(const float *T, bf16 *Tc, float *scale, int dk, int64_t n_pairs, hipStream_t st);
 
 // Re-rotation of cached pairs to absolute offsets (rotary embeddings): item i
 // reads slot slot[i] and writes (R T R^T, R S) at offset offset[i] to item i.

@@ -116,6 +116,48 @@ k_conv_warmup(ConvArgs a) {
     }
 }
 
+// Compact pairs: one workgroup per (slot, chain) finds max |T| and writes
+// T^ = T / sigma in bf16 with sigma = 2^e, max |T| = m 2^e, m in [0.5, 1), so
+// that |T^| < 1 and the division is exact; T = 0 (or not finite) keeps
+// sigma = 1.
+__global__ void __launch_bounds__(VAR_THREADS)
+k_pair_compact(const float *T, bf16 *Tc, float *scale, int dk) {
+    __shared__ float wmax[VAR_THREADS / 64];
+    const int64_t p = blockIdx.x;
+    const float *t = T + p * dk * dk;
+    bf16 *tc = Tc + p * dk * dk;
+    const int n4 = dk * dk / 4, tid = threadIdx.x;
+    float mx = 0.f;
+    for (int i = tid; i < n4; i += VAR_THREADS) {
+        const f32x4 v = reinterpret_cast<const f32x4 *>(t)[i];
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if ((tid & 63) == 0) wmax[tid >> 6] = mx;
+    __syncthreads();
+    mx = wmax[0];
+#pragma unroll
+    for (int w = 1; w < VAR_THREADS / 64; ++w) mx = fmaxf(mx, wmax[w]);
+    int e = 0;
+    if (mx > 0.f && isfinite(mx)) frexpf(mx, &e);
+    if (tid == 0) scale[p] = ldexpf(1.f, e);
+    for (int i = tid; i < n4; i += VAR_THREADS) {
+        const f32x4 v = reinterpret_cast<const f32x4 *>(t)[i];
+        bf16x4 h;
+        // (ldexp, not a product with 2^-e: for a T in fp32's subnormal range
+        // 2^-e itself overflows)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) h[k] = (bf16)ldexpf(v[k], -e);
+        reinterpret_cast<bf16x4 *>(tc)[i] = h;
+    }
+}
+
+hipError_t pair_compact(const float *T, bf16 *Tc, float *scale, int dk, int64_t n_pairs, hipStream_t st) {
+    hipLaunchKernelGGL(k_pair_compact, dim3((unsigned)n_pairs), dim3(VAR_THREADS), 0, st, T, Tc, scale, dk);
+    return hipGetLastError();
+}
+
 hipError_t rerotate(const RerotateArgs &a, int n_items, hipStream_t st) {
     hipLaunchKernelGGL(k_rerotate, dim3((unsigned)((int64_t)n_items * a.n_chains)), dim3(VAR_THREADS), 0, st, a);
     return hipGetLastError();

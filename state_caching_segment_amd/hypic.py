@@ -26,7 +26,7 @@ STATUS = {0: "HYPIC_OK", -1: "HYPIC_E_INVALID", -2: "HYPIC_E_UNSUPPORTED", -3: "
           -4: "HYPIC_E_DEVICE"}
 EXPORTS = ("hypic_t_elems", "hypic_workspace_bytes", "hypic_segment_build", "hypic_segment_prefill",
            "hypic_compose", "hypic_compose_tree_noalloc", "hypic_seam_advance", "hypic_rerotate",
-           "hypic_conv_warmup", "hypic_store_create", "hypic_store_destroy", "hypic_store_acquire",
+           "hypic_conv_warmup", "hypic_pair_compact", "hypic_compose_compact", "hypic_store_create", "hypic_store_destroy", "hypic_store_acquire",
            "hypic_store_evict", "hypic_store_stats", "hypic_content_key", "hypic_status_string", "hypic_last_error")
 NOALLOC_WORKSPACE_BYTES = 64 << 20  # HYPIC_NOALLOC_WORKSPACE_BYTES
 
@@ -82,6 +82,10 @@ def load(path: str = LIB_PATH, cache: bool = True) -> ctypes.CDLL:
     lib.hypic_rerotate.restype = ctypes.c_int
     lib.hypic_conv_warmup.argtypes = [P, P, P, i32, i32, i32, P, i32, P, P, P, P]
     lib.hypic_conv_warmup.restype = ctypes.c_int
+    lib.hypic_pair_compact.argtypes = [P, i32, P, P, P, P]
+    lib.hypic_pair_compact.restype = ctypes.c_int
+    lib.hypic_compose_compact.argtypes = [P, i32, i32, P, P, i64, P, P, P, P, P, i32, P, P, P, P]
+    lib.hypic_compose_compact.restype = ctypes.c_int
     lib.hypic_store_create.argtypes = [i64]
     lib.hypic_store_create.restype = P
     lib.hypic_store_destroy.argtypes = [P]
@@ -205,6 +209,18 @@ def hypic_conv_warmup(L: hypic_layout, raw: hypic_tokens, taps, conv_k: int, act
                       w: int, q_out, k_out, v_out, stream=None) -> None:
     _check(load().hypic_conv_warmup(ctypes.byref(L), ctypes.byref(raw), _p(taps), conv_k, act, n_items,
                                     _p(tok_begin), w, _p(q_out), _p(k_out), _p(v_out), _stream(stream)))
+
+
+def hypic_pair_compact(L: hypic_layout, n_slots: int, T, Tc, Tscale, stream=None) -> None:
+    _check(load().hypic_pair_compact(ctypes.byref(L), n_slots, _p(T), _p(Tc), _p(Tscale), _stream(stream)))
+
+
+def hypic_compose_compact(L: hypic_layout, n_req: int, max_list_len: int, list_off, pair_id, n_slots: int, Tc,
+                          Tscale, S, seam: Optional[hypic_tokens], seam_begin, w: int, state, o, prefix_states=None,
+                          stream=None) -> None:
+    _check(load().hypic_compose_compact(ctypes.byref(L), n_req, max_list_len, _p(list_off), _p(pair_id), n_slots,
+                                        _p(Tc), _p(Tscale), _p(S), ctypes.byref(seam) if seam is not None else None,
+                                        _p(seam_begin), w, _p(state), _p(o), _p(prefix_states), _stream(stream)))
 
 
 class Store:

@@ -96,6 +96,10 @@ def dense_T(Tc: np.ndarray, dk: int) -> np.ndarray:
 
 
 def _rel(x, ref):
+    # a non-finite value (an unwritten NaN output, an overflow) is an infinite
+    # error: max() over objects would silently pass over a NaN
+    if not np.isfinite(x).all():
+        return float("inf")
     nr = np.linalg.norm(ref)
     return float(np.linalg.norm(x - ref) / nr) if nr > 0 else float(np.linalg.norm(x))
 
