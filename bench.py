@@ -419,8 +419,8 @@ def main():
                     help="layers to run one after another, each on fresh inputs generated untimed (workloads "
                          "with cache hits); the per-layer times and their sum are reported")
     ap.add_argument("--no-prefill", action="store_true", help="skip the fused cold prefill leg")
-    ap.add_argument("--ab", default=None, metavar="LIB",
-                    help="another build of libhypic.so: steps alternate between the two in this process")
+    ap.add_argument("--ab", default=None, metavar="LIB[,LIB...]",
+                    help="other builds of libhypic.so: steps alternate between this one and them in this process")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path shards by chain with no "
@@ -442,7 +442,7 @@ def main():
     lib_a = hy.load()
     libs = None
     if args.ab:
-        libs = [lib_a, hy.hypic.load(os.path.abspath(args.ab), cache=False)]
+        libs = [lib_a] + [hy.hypic.load(os.path.abspath(p), cache=False) for p in args.ab.split(",")]
     stream = torch.cuda.current_stream()
     copy_bw = copy_bandwidth(stream)
 
@@ -511,9 +511,9 @@ def main():
         "hbm_copy_measured_GBps": copy_bw / 1e9,
     }
     if libs:
-        (bb_ms, cb_ms), = ab
-        out["ab"] = {"lib": args.ab, "build_ms": [float(np.median(b_ms)), float(np.median(bb_ms))],
-                     "compose_ms": [float(np.median(c_ms)), float(np.median(cb_ms))]}
+        out["ab"] = {"libs": ["this"] + args.ab.split(","),
+                     "build_ms": [float(np.median(b_ms))] + [float(np.median(x[0])) for x in ab],
+                     "compose_ms": [float(np.median(c_ms))] + [float(np.median(x[1])) for x in ab]}
     # fused cold prefill of the same bodies (outputs of every body token and the pairs)
     if not args.no_prefill and wl.family in ("deltanet", "gdn") and wl.dtype == "bf16":
         pout = torch.empty(wl.n_tok, C, d, dtype=wl.k.dtype, device="cuda")

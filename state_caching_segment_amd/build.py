@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhypic.so")
 SOURCES = ["api.cpp", "build_dense.hip", "build_dense_pipe.hip", "build_kda.hip", "build_diag.hip", "compose.hip",
-           "variants.hip", "store.cpp"]
+           "variants.hip", "store.cpp", "build_kda_pipe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -293,7 +293,9 @@ int hypic_segment_build(const hypic_layout *L, const hypic_tokens *x, int32_t n_
     a.S = d_S;
     const int D = padded_d(L->dk);
     const bool bf = L->in_dtype == HYPIC_BF16;
-    if (L->family == HYPIC_KDA) return launched(hy::build_kda(a, bf, D, n_seg, st), "KDA build launch");
+    if (L->family == HYPIC_KDA)
+        return launched(bf ? hy::build_kda_pipe(a, D, n_seg, st) : hy::build_kda(a, bf, D, n_seg, st),
+                        "KDA build launch");
     if (dense(L->family)) {
         if (bf) return launched(hy::build_dense_pipe(a, L->family, D, n_seg, st), "dense build launch");
         return launched(hy::build_dense(a, L->family, bf, D, n_seg, st), "dense build launch");

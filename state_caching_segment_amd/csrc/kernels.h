@@ -63,6 +63,7 @@ struct TreeArgs {
 hipError_t build_dense(const BuildArgs &a, int family, bool bf16_in, int D, int n_seg, hipStream_t st);
 hipError_t build_dense_pipe(const BuildArgs &a, int family, int D, int n_seg, hipStream_t st);
 hipError_t build_kda(const BuildArgs &a, bool bf16_in, int D, int n_seg, hipStream_t st);
+hipError_t build_kda_pipe(const BuildArgs &a, int D, int n_seg, hipStream_t st);  // bf16 inputs
 hipError_t build_diag(const BuildArgs &a, int family, bool bf16_in, int D, int n_seg, hipStream_t st);
 hipError_t compose_seq(const ComposeArgs &a, int family, bool bf16_in, int D, int n_req, hipStream_t st);
 hipError_t compose_tree(const TreeArgs &t, int family, bool bf16_in, int D, int n_req, hipStream_t st);

@@ -120,3 +120,30 @@ def chunk_pair_folded(fam, k, v, g=None, beta=None, c=64, blk=16):
             R[b0:b1] = acc
         X = lam * X + K.T @ R
     return X[:, :dk], X[:, dk:]
+
+
+def chunk_pair_kda_inv(k, v, g, beta, c=32):
+    """The per-channel form of the bf16 KDA build: with K_L rows
+    exp(Gam_t) * k_t and K_i rows exp(-Gam_t) * k_t (per channel),
+        G = tril(K_L K_i^T, -1)       (no per-block reference token)
+        A = (I + diag(beta) G)^-1 diag(beta)
+        R = A ([0 | V] - K_L X)
+        X <- diag(exp(Gam_c)) (X + K_i^T R)
+    which is diag(exp Gam_c) X + Kt^T R with Kt = diag-scaled K_i."""
+    k, v = np.asarray(k, np.float64), np.asarray(v, np.float64)
+    n, dk = k.shape
+    dv = v.shape[1]
+    lg = np.asarray(g, np.float64).reshape(n, dk)
+    bb = np.asarray(beta, np.float64)
+    X = np.concatenate([np.eye(dk), np.zeros((dk, dv))], axis=1)
+    for s in range(0, n, c):
+        e = min(n, s + c)
+        L = e - s
+        K, V, b = k[s:e], v[s:e], bb[s:e]
+        Gm = np.cumsum(lg[s:e], axis=0)
+        Kl, Ki = np.exp(Gm) * K, np.exp(-Gm) * K
+        G = np.tril(Kl @ Ki.T, -1)
+        A = np.linalg.solve(np.eye(L) + np.diag(b) @ G, np.diag(b))
+        R = A @ (np.concatenate([np.zeros((L, dk)), V], axis=1) - Kl @ X)
+        X = np.exp(Gm[-1])[:, None] * (X + Ki.T @ R)
+    return X[:, :dk], X[:, dk:]

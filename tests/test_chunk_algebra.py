@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 import oracle
-from chunk_model import chunk_pair, chunk_pair_folded, chunk_run
+from chunk_model import chunk_pair, chunk_pair_folded, chunk_pair_kda_inv, chunk_run
 
 FAMS = ["linear", "retnet", "mamba2", "gla", "deltanet", "gdn", "kda"]
 
@@ -73,3 +73,18 @@ def test_gdn_transition_is_decay_times_deltanet():
         T, _ = oracle.pair("gdn", k, v, g, beta)
         Tu, _ = oracle.pair("deltanet", k, v, None, beta)
         assert oracle.rel_fro(np.exp(g.sum()) * Tu, T) < 1e-12, n
+
+
+@pytest.mark.parametrize("law", ["c5", "strong"])
+def test_kda_inverse_decay_form_matches_oracle(law):
+    """The bf16 KDA build's form (Gram as K_L K_i^T without reference tokens,
+    update as diag(exp Gam_c)(X + K_i^T R)) equals the oracle, also with
+    per-channel gates strong enough that exp(-Gam) reaches e^60 in a chunk."""
+    rng = np.random.default_rng(140 + (law == "strong"))
+    for n in (1, 17, 32, 33, 150):
+        q, k, v, g, beta, gamma = _inputs(rng, "kda", n, 8, 6)
+        if law == "strong":
+            g = -np.log1p(np.exp(rng.normal(0.5, 0.3, size=(n, 8))))   # about -1 per token
+        T, S = oracle.pair("kda", k, v, g, beta)
+        Tc, Sc = chunk_pair_kda_inv(k, v, g, beta)
+        assert oracle.rel_fro(Tc, T) < 1e-10 and oracle.rel_fro(Sc, S) < 1e-10, (n, law)
