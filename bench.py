@@ -64,7 +64,7 @@ def _t_elems(family, d):
 def build_cost(family, lens, d, n_chains, in_bytes):
     """Algorithmic flops and HBM bytes of building the pairs of segments with
     the given lengths.
-    Dense families (chunked UT/WY form, c = 64), per chunk of c tokens: carry
+    Dense families (chunked UT/WY form, c = 64; KDA c = 32), per chunk of c tokens: carry
     of [T|S] 8 c d^2 (4 c d^2 for a segment's first chunk, which starts from
     [I|0]), Gram c(c-1)d, unit-lower inverse c^3/3, W and U 2 c^2 d.
     Diagonal families: 2 d^2 per token (the k~ v^T accumulation).
@@ -73,8 +73,9 @@ def build_cost(family, lens, d, n_chains, in_bytes):
     flops = 0.0
     for n in lens:
         if family in DENSE:
-            for j, c0 in enumerate(range(0, int(n), CH)):
-                c = min(CH, int(n) - c0)
+            ch = 32 if family == "kda" else CH
+            for j, c0 in enumerate(range(0, int(n), ch)):
+                c = min(ch, int(n) - c0)
                 carry = 8 * c * d * d if j > 0 else 4 * c * d * d
                 flops += carry + c * (c - 1) * d + c ** 3 / 3 + 2 * c * c * d
         else:
@@ -102,6 +103,8 @@ def build_kernel(family, dtype):
     """The build kernel the library dispatches for a family and input dtype,
     and the sources whose hash keys its stored counter readings."""
     if family == "kda":
+        if dtype == "bf16":
+            return "k_build_kda_pipe", ["build_kda_pipe.hip", "common.h"]
         return "k_build_kda", ["build_kda.hip", "common.h"]
     if family in ("deltanet", "gdn"):
         if dtype == "bf16":
