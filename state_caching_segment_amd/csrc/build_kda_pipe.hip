@@ -56,7 +56,7 @@ struct KpCfg {
     static constexpr int offA = 3 * STAGE;
     static constexpr int ABUF = al(2 * KPC * LDA * 2);
     // solver scratch
-    static constexpr int LDL = KPC + 1, LDI = KPC + 4;
+    static constexpr int LDL = KPC + 4, LDI = KPC + 4;  // 16-byte aligned rows
     static constexpr int offL = offA + 2 * ABUF;
     static constexpr int offInv = offL + al(KPC * LDL * 4);
     static constexpr int total = offInv + al(KPC * LDI * 4);
@@ -141,21 +141,36 @@ k_build_kda_pipe(BuildArgs a) {
                 }
             }
             kp_wave_fence();
-            // (I + L)^-1: the two diagonal 16 x 16 blocks by forward
-            // substitution (lane = column, one block per lane group), zeros in
-            // the upper right
+            // (I + L)^-1: the two diagonal 16 x 16 blocks, one row r16 per lane
+            // (block grp): y (I + L_bb) = e_r, swept from the last row up; once
+            // y_i is final its multiple of row i of L_bb leaves every y_j,
+            // j < i, so the dependent chain is 16 steps, each row read as four
+            // vectors one step ahead.  Zeros in the upper right.
             if (grp < 2) {
-                const int bk = grp, col = r16;
-                float xr[16];
+                const float *Lb = sL + 16 * grp * LDL + 16 * grp;
+                float y[16];
 #pragma unroll
-                for (int rr = 0; rr < 16; ++rr) {
-                    float s = (rr == col) ? 1.f : 0.f;
+                for (int j = 0; j < 16; ++j) y[j] = (j == r16) ? 1.f : 0.f;
+                f32x4 cur[4], nxt[4];
 #pragma unroll
-                    for (int j = 0; j < rr; ++j) s -= sL[(16 * bk + rr) * LDL + 16 * bk + j] * xr[j];
-                    xr[rr] = s;
+                for (int q = 0; q < 4; ++q) cur[q] = *reinterpret_cast<const f32x4 *>(Lb + 15 * LDL + 4 * q);
+#pragma unroll
+                for (int i = 15; i > 0; --i) {
+#pragma unroll
+                    for (int q = 0; 4 * q < i - 1; ++q)
+                        nxt[q] = *reinterpret_cast<const f32x4 *>(Lb + (i - 1) * LDL + 4 * q);
+#pragma unroll
+                    for (int q = 0; 4 * q < i; ++q)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (4 * q + e < i) y[4 * q + e] -= y[i] * cur[q][e];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
                 }
+                float *Ib = sInv + (16 * grp + r16) * LDI + 16 * grp;
 #pragma unroll
-                for (int rr = 0; rr < 16; ++rr) sInv[(16 * bk + rr) * LDI + 16 * bk + col] = xr[rr];
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<f32x4 *>(Ib + 4 * q) = f32x4{y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]};
             } else {
                 for (int e = lane - 32; e < 256; e += 32) sInv[(e >> 4) * LDI + 16 + (e & 15)] = 0.f;
             }
@@ -241,12 +256,12 @@ k_build_kda_pipe(BuildArgs a) {
         for (int e = 0; e < 8; ++e) {
             const float G = half_incl_scan((float)gpre[e] * KP_L2E);  // log2 units, tokens 0 .. t
             const float kv = (float)kpre[e];
-            kl[e] = kv * __builtin_amdgcn_exp2f(G);
+            const float eg = __builtin_amdgcn_exp2f(G);
+            kl[e] = kv * eg;
             ki[e] = kv * __builtin_amdgcn_exp2f(-G);
-            // the chunk's total decay: the half-wave's last lane
-            const float Gc = __builtin_bit_cast(
-                float, __builtin_amdgcn_ds_bpermute(4 * ((ln & 32) | 31), __builtin_bit_cast(int, G)));
-            if (t == KPC - 1) lam[i8 + e] = __builtin_amdgcn_exp2f(Gc);
+            // the chunk's total decay is the last token's (tokens past a
+            // ragged end carry zero log-gates)
+            if (t == KPC - 1) lam[i8 + e] = eg;
             VT[(i8 + e) * LDV + t] = vpre[e];
         }
         bf16x8 h, l;
@@ -273,7 +288,16 @@ k_build_kda_pipe(BuildArgs a) {
         if (nch > 1) prefetch(1);
         __syncthreads();
     }
+    // The two carry waves of a SIMD take the window's two jobs in opposite
+    // orders (T waves carry then stage, S waves stage then carry), so that
+    // one wave's staging arithmetic issues beside the other's matrix work.
+    // The staging of chunk c + 2 does not depend on the carry of chunk c.
     for (int c = -1; c < nch; ++c) {
+        if (isS && c + 2 < nch) {
+            stage_chunk(c + 2);
+            if (c + 3 < nch) prefetch(c + 3);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         if (c >= 0) {
             const char *st = stage(c);
             const bf16 *KLh = reinterpret_cast<const bf16 *>(st + Cfg::sKLh);
@@ -367,7 +391,7 @@ k_build_kda_pipe(BuildArgs a) {
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (c + 2 < nch) {
+        if (!isS && c + 2 < nch) {
             stage_chunk(c + 2);
             if (c + 3 < nch) prefetch(c + 3);
         }
