@@ -15,6 +15,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "compose_common.h"
 
 namespace hy {
 
@@ -289,31 +290,53 @@ k_build_diag_slices(BuildArgs a) {
     // staging role: channels ch, ch + 1 and tokens 8 tq .. 8 tq + 7 of the chunk
     const int tq = lane >> 4, ch = 32 * q + 2 * (lane & 15);
     const bool ch_ok = ch < dk;
-    const int chc = ch_ok ? ch : 0;
-    const bf16 *kp = reinterpret_cast<const bf16 *>(a.x.k) + (int64_t)chain * a.x.cs + chc;
-    const bf16 *vp = reinterpret_cast<const bf16 *>(a.x.v) + (int64_t)chain * a.x.cs + chc;
-    const bf16 *gp = (VG || FAM == MAMBA2)
-                         ? reinterpret_cast<const bf16 *>(a.x.g) + (int64_t)chain * a.x.gcs + (VG ? chc : 0)
-                         : nullptr;
+    const bf16 *kb = reinterpret_cast<const bf16 *>(a.x.k) + (int64_t)chain * a.x.cs;
+    const bf16 *vb = reinterpret_cast<const bf16 *>(a.x.v) + (int64_t)chain * a.x.cs;
+    const bf16 *gb = (VG || FAM == MAMBA2) ? reinterpret_cast<const bf16 *>(a.x.g) + (int64_t)chain * a.x.gcs : nullptr;
     const float lgam = FAM == RETNET ? logf(a.x.gamma[chain]) * L2E : 0.f;
+    // Loads go through a buffer view of the chunk's valid tokens, so tokens
+    // past the segment's end (and a chunk outside the segment) read as zeros:
+    // zero k and v add nothing and a zero log-gate decays nothing.  The token
+    // offsets sit in the per-lane offset, which the view's range check covers
+    // (the scalar offset is not checked).  Lanes past dk read out of range.
+    // Offsets stay below 2^31: token strides are at most 2^24 elements.
+    const int ts2 = (int)a.x.ts * 2, gts2 = (int)a.x.gts * 2;
+    constexpr int OOR = 0x40000000;  // beyond any chunk view (32 tokens x 2^25 bytes)
+    const int voff = ch_ok ? 8 * tq * ts2 + 2 * ch : OOR;
+    const int goff = VG ? (ch_ok ? 8 * tq * gts2 + 2 * ch : OOR) : 8 * tq * gts2;
 
     typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
     bf16x2 pk[8], pv[8], pg[8];
     bf16 pgs[8];
-    int pvalid = 0;  // bit j: token 8 tq + j of the prefetched chunk exists
-    // chunk gc of the segment into the prefetch registers (unconditional loads
-    // from clamped tokens, masked when used)
+    int pvalid = 0;  // (RetNet) bit j: token 8 tq + j of the prefetched chunk exists
+    // chunk gc of the segment into the prefetch registers
     auto fetch = [&](int gc) {
-        pvalid = 0;
+        const int64_t c0 = (int64_t)gc * CS;
+        const int L = (gc >= 0 && gc < nch) ? (int)(n - c0 < CS ? n - c0 : CS) : 0;
+        const int64_t tb = b0 + (L > 0 ? c0 : 0);
+        const auto rk = buffer_view(kb + tb * a.x.ts, L * ts2);
+        const auto rv = buffer_view(vb + tb * a.x.ts, L * ts2);
+        if (FAM == RETNET) {
+            pvalid = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (8 * tq + j < L && ch_ok) pvalid |= 1 << j;
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int64_t tok = (int64_t)gc * CS + 8 * tq + j;
-            if (gc >= 0 && gc < nch && tok < n && ch_ok) pvalid |= 1 << j;
-            const int64_t tc = b0 + (tok < n ? (tok >= 0 ? tok : 0) : (n > 0 ? n - 1 : 0));
-            pk[j] = *reinterpret_cast<const bf16x2 *>(kp + tc * a.x.ts);
-            pv[j] = *reinterpret_cast<const bf16x2 *>(vp + tc * a.x.ts);
-            if (VG) pg[j] = *reinterpret_cast<const bf16x2 *>(gp + tc * a.x.gts);
-            if (FAM == MAMBA2) pgs[j] = gp[tc * a.x.gts];
+            pk[j] = __builtin_bit_cast(bf16x2, __builtin_amdgcn_raw_buffer_load_b32(rk, voff + j * ts2, 0, 0));
+            pv[j] = __builtin_bit_cast(bf16x2, __builtin_amdgcn_raw_buffer_load_b32(rv, voff + j * ts2, 0, 0));
+        }
+        if constexpr (VG || FAM == MAMBA2) {
+            const auto rg = buffer_view(gb + tb * a.x.gts, L * gts2);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (VG)
+                    pg[j] = __builtin_bit_cast(bf16x2, __builtin_amdgcn_raw_buffer_load_b32(rg, goff + j * gts2, 0, 0));
+                else
+                    pgs[j] = __builtin_bit_cast(
+                        bf16, (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(rg, goff + j * gts2, 0, 0));
+            }
         }
     };
 
@@ -335,8 +358,8 @@ k_build_diag_slices(BuildArgs a) {
         bf16 *sV = reinterpret_cast<bf16 *>(gb + Cfg::gV);
         // ---- this lane's quarter: product of its 8 tokens' gates per channel
         auto gate = [&](int j, int e) -> float {
-            if (!(pvalid & (1 << j))) return 0.f;
-            return VG ? (float)pg[j][e] * L2E : (FAM == MAMBA2 ? (float)pgs[j] * L2E : lgam);
+            if (FAM == RETNET) return (pvalid & (1 << j)) ? lgam : 0.f;
+            return VG ? (float)pg[j][e] * L2E : (float)pgs[j] * L2E;
         };
         float P[2] = {1.f, 1.f};
         if (DEC) {
@@ -363,17 +386,16 @@ k_build_diag_slices(BuildArgs a) {
         float W[2] = {E[0], E[1]};
 #pragma unroll
         for (int j = 7; j >= 0; --j) {
-            const bool ok = pvalid & (1 << j);
             float kv[2];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                kv[e] = ok ? (float)pk[j][e] * W[e] : 0.f;
+                kv[e] = (float)pk[j][e] * W[e];
                 if (DEC) W[e] *= __builtin_amdgcn_exp2f(gate(j, e));
             }
             const bf16 h0 = (bf16)kv[0], h1 = (bf16)kv[1];
             const bf16x2 hh = {h0, h1};
             const bf16x2 ll = {(bf16)(kv[0] - (float)h0), (bf16)(kv[1] - (float)h1)};
-            const bf16x2 vv = ok ? pv[j] : bf16x2{(bf16)0.f, (bf16)0.f};
+            const bf16x2 vv = pv[j];
             const int o = (8 * tq + j) * LDK + ch;
             *reinterpret_cast<bf16x2 *>(sK + o) = hh;
             if (DEC) *reinterpret_cast<bf16x2 *>(sKl + o) = ll;
