@@ -110,7 +110,9 @@ def build_kernel(family, dtype):
         if dtype == "bf16":
             return "k_build_dense_pipe", ["build_dense_pipe.hip", "common.h"]
         return "k_build_dense", ["build_dense.hip", "common.h"]
-    return "k_build_diag", ["build_diag.hip", "common.h"]
+    if dtype == "bf16":
+        return "k_build_diag_slices", ["build_diag.hip", "common.h", "compose_common.h"]
+    return "k_build_diag", ["build_diag.hip", "common.h", "compose_common.h"]
 
 
 def compose_kernel(family, in_bf16=True, d=128, tree=False):
