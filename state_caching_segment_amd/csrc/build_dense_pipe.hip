@@ -151,7 +151,7 @@ __device__ __forceinline__ void wave_lds_fence() {
 // t0 .. t0 + min(L, 64) - 1, from the chunk-start state X (its S columns), the
 // solved R' (split, C layout per 16-row block) and the staged blocks of
 // tril(Q K^T); one 16-column half at a time, which bounds the registers held.
-template <int D, typename Cfg>
+template <int D, typename Cfg, int NT0>
 __device__ __forceinline__ void prefill_out(const f32x4 (&X)[D / 16][2], const s4 (&Rh)[4][2], const s4 (&Rl)[4][2],
                                             const char *buf, const BuildArgs &a, int64_t t0, int L, int chain, int c0) {
     constexpr int KB = D / 32, LDK = Cfg::LDK, TILE = Cfg::TILE;
@@ -161,7 +161,7 @@ __device__ __forceinline__ void prefill_out(const f32x4 (&X)[D / 16][2], const s
     const float *bE = reinterpret_cast<const float *>(buf + Cfg::bE);
     bf16 *o = reinterpret_cast<bf16 *>(a.o) + (int64_t)chain * a.ocs + c0 + r16;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = NT0; nt < 2; ++nt) {
         // P = Q S0 on this half's columns (the state split hi + lo; q exact in bf16)
         f32x4 P[4];
 #pragma unroll
@@ -448,15 +448,20 @@ k_build_dense_pipe(BuildArgs a) {
     }
 
     const int lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+    // Columns of [T | S] per wave.  Plain build: wave wv holds columns
+    // 32 wv .. 32 wv + 31.  Prefill: tile 0 holds T columns 16 wv .. 16 wv + 15
+    // and tile 1 the same columns of S, so that every carry wave writes the
+    // outputs of 16 columns (the outputs cost as much as the carry of S).
     const int cbase = wv * 32;
     const bool isS = cbase >= D;
+    auto col0 = [&](int nt) { return PF ? (nt ? D : 0) + 16 * wv : cbase + 16 * nt; };
     f32x4 X[RT][2];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) X[rt][nt][jj] = (16 * rt + 4 * grp + jj == cbase + 16 * nt + r16) ? 1.f : 0.f;
+            for (int jj = 0; jj < 4; ++jj) X[rt][nt][jj] = (16 * rt + 4 * grp + jj == col0(nt) + r16) ? 1.f : 0.f;
     if (nch > 0) __syncthreads();
     for (int c = 0; c < nch; ++c) {
         const char *buf = smem + (c & 1) * Cfg::BUF;
@@ -498,9 +503,9 @@ k_build_dense_pipe(BuildArgs a) {
             for (int nt = 0; nt < 2; ++nt) {
                 f32x4 y = -lam * Z[mt][nt];
                 if constexpr (PF) {
-                    if (isS) {
+                    if (nt == 1) {
                         const bf16x4 v4 = *reinterpret_cast<const bf16x4 *>(
-                            reinterpret_cast<const bf16 *>(buf + Cfg::bV) + (cbase - D + 16 * nt + r16) * LDVB + 16 * mt +
+                            reinterpret_cast<const bf16 *>(buf + Cfg::bV) + (16 * wv + r16) * LDVB + 16 * mt +
                             4 * grp);
                         const f32x4 e4 = *reinterpret_cast<const f32x4 *>(
                             reinterpret_cast<const float *>(buf + Cfg::bE) + 16 * mt + 4 * grp);
@@ -533,8 +538,8 @@ k_build_dense_pipe(BuildArgs a) {
             for (int nt = 0; nt < 2; ++nt) split4(r[nt], Rh[b][nt], Rl[b][nt]);
         }
         if constexpr (PF) {
-            if (isS) prefill_out<D, Cfg>(X, Rh, Rl, buf, a, b0 + (int64_t)c * CH, (int)(n - (int64_t)c * CH), chain,
-                                         cbase - D);
+            prefill_out<D, Cfg, 1>(X, Rh, Rl, buf, a, b0 + (int64_t)c * CH, (int)(n - (int64_t)c * CH), chain,
+                                   16 * wv - 16);
         }
         // X = lambda X + K^T R'
         if (FAM == GDN) {
@@ -573,8 +578,9 @@ k_build_dense_pipe(BuildArgs a) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int row = 16 * rt + 4 * grp + jj;
-                const int col = cbase + 16 * nt + r16 - (isS ? D : 0);
-                if (row < dk && col < dk) (isS ? So : To)[row * dk + col] = X[rt][nt][jj];
+                const bool s_ = col0(nt) >= D;
+                const int col = col0(nt) + r16 - (s_ ? D : 0);
+                if (row < dk && col < dk) (s_ ? So : To)[row * dk + col] = X[rt][nt][jj];
             }
 }
 

@@ -4,8 +4,9 @@ against the fp64 oracle's token-by-token recurrence over the same tokens.
 
 Per object: the n x dv output block of each (segment, chain) and its T and S,
 relative Frobenius error <= 5e-3 (bf16 inputs, fp32 state, bf16 outputs).  The
-pair must also be the one hypic_segment_build writes (T bitwise, S to
-rounding): the same chunk arithmetic runs in both."""
+pair must also agree with the one hypic_segment_build writes to fp32 rounding
+(relative 1e-4 for T and 1e-5 for S per segment): the same chunk arithmetic
+runs in both."""
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -37,11 +38,15 @@ def _prefill(wl, plan):
     T2, S2 = torch.empty_like(T), torch.empty_like(S)
     hy.hypic_segment_build(L, x, plan.n_slots, sb, se, plan.max_seg_len, T2, S2)
     torch.cuda.synchronize()
-    # T is carried by the same waves with the same arithmetic: bitwise equal.
-    # S rounds e^{Gamma_c - Gamma_t} v_t once less in the prefill (the decay
-    # is applied where the value is consumed), so it agrees to rounding.
-    assert torch.equal(T, T2), "prefill T differs from the build's"
-    assert float((S - S2).double().norm() / S2.double().norm()) < 1e-5
+    # The same chunk arithmetic with another assignment of columns to waves
+    # (and S rounds e^{Gamma_c - Gamma_t} v_t once less in the prefill: the
+    # decay is applied where the value is consumed): both pairs agree to fp32
+    # rounding, segment by segment; a long segment's T, the product of all its
+    # transitions, accumulates the most (1e-4 relative; S 1e-5).
+    for s in range(plan.n_slots):
+        for a, b, tol in ((T[s], T2[s], 1e-4), (S[s], S2[s], 1e-5)):
+            assert torch.isfinite(a).all()
+            assert float((a - b).double().norm()) <= tol * float(b.double().norm()) + 1e-30, s
     return T, S, out
 
 
