@@ -62,6 +62,11 @@
  *   - HYPIC_FAULT_INJECT ("1" or "all"; or "build", "compose", "seam",
  *     "rerotate", "conv", "compact" for one call): after its arguments have been validated, the call returns
  *     HYPIC_E_DEVICE and enqueues nothing.  For testing callers' error paths.
+ *   - HYPIC_DEBUG (any value but "0"): every call synchronizes `stream`
+ *     after its launch, so that an error in the kernel's execution returns
+ *     HYPIC_E_DEVICE from the call that launched it, naming the launch in
+ *     hypic_last_error() (without it, such an error surfaces at the caller's
+ *     next synchronization).  Calls become synchronous.
  *   - dv must equal dk (HYPIC_E_UNSUPPORTED otherwise): every kernel keeps the
  *     state and T in tiles of the same width, and every workload these
  *     kernels are sized for has dk == dv.

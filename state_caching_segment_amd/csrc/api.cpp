@@ -103,8 +103,23 @@ hy::Tok to_tok(const hypic_tokens *x) {
     return t;
 }
 
-int launched(hipError_t e, const char *what) {
+// HYPIC_DEBUG=1: every call synchronizes its stream after launching, so that
+// an error in the kernel's execution is reported by the call that launched
+// it, with the launch's name (normally it surfaces at the caller's next
+// synchronization, from whichever call that is).
+bool debug_on() {
+    const char *e = getenv("HYPIC_DEBUG");
+    return e && e[0] && strcmp(e, "0") != 0;
+}
+
+int launched(hipError_t e, const char *what, hipStream_t st) {
     if (e != hipSuccess) return fail(HYPIC_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+    if (debug_on()) {
+        e = hipStreamSynchronize(st);
+        if (e == hipSuccess) e = hipGetLastError();
+        if (e != hipSuccess) return fail(HYPIC_E_DEVICE, "%s (HYPIC_DEBUG, at the stream synchronization): %s", what,
+                                         hipGetErrorString(e));
+    }
     return ok();
 }
 
@@ -295,12 +310,12 @@ int hypic_segment_build(const hypic_layout *L, const hypic_tokens *x, int32_t n_
     const bool bf = L->in_dtype == HYPIC_BF16;
     if (L->family == HYPIC_KDA)
         return launched(bf ? hy::build_kda_pipe(a, D, n_seg, st) : hy::build_kda(a, bf, D, n_seg, st),
-                        "KDA build launch");
+                        "KDA build launch", st);
     if (dense(L->family)) {
-        if (bf) return launched(hy::build_dense_pipe(a, L->family, D, n_seg, st), "dense build launch");
-        return launched(hy::build_dense(a, L->family, bf, D, n_seg, st), "dense build launch");
+        if (bf) return launched(hy::build_dense_pipe(a, L->family, D, n_seg, st), "dense build launch", st);
+        return launched(hy::build_dense(a, L->family, bf, D, n_seg, st), "dense build launch", st);
     }
-    return launched(hy::build_diag(a, L->family, bf, D, n_seg, st), "diagonal build launch");
+    return launched(hy::build_diag(a, L->family, bf, D, n_seg, st), "diagonal build launch", st);
 }
 
 }  // extern "C"
@@ -359,7 +374,7 @@ int compose_call(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t max
         (rc = validate_lists(n_req, max_list_len, d_list_off, d_pair_id, n_slots, has_seam ? d_seam_begin : nullptr, st)))
         return rc;
     if ((rc = injected("compose"))) return rc;
-    if (mode == HYPIC_SEQ) return launched(hy::compose_seq(a, L->family, bf, padded_d(L->dk), n_req, st), "compose launch");
+    if (mode == HYPIC_SEQ) return launched(hy::compose_seq(a, L->family, bf, padded_d(L->dk), n_req, st), "compose launch", st);
     if (max_list_len == 0) return ok();
     if (lib_ws) {
         const hipError_t e = hy::static_workspace(&d_ws);
@@ -376,7 +391,7 @@ int compose_call(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t max
     t.sin = reinterpret_cast<float *>(base + tl.off_sin);
     t.pvec = reinterpret_cast<float *>(base + tl.off_pvec);
     t.blk_off = reinterpret_cast<int32_t *>(base + tl.off_blk);
-    return launched(hy::compose_tree(t, L->family, bf, padded_d(L->dk), n_req, st), "tree compose launch");
+    return launched(hy::compose_tree(t, L->family, bf, padded_d(L->dk), n_req, st), "tree compose launch", st);
 }
 
 }  // namespace
@@ -414,7 +429,7 @@ int hypic_segment_prefill(const hypic_layout *L, const hypic_tokens *x, int32_t 
     a.o = d_out;
     a.ots = out_tok_stride;
     a.ocs = out_chain_stride;
-    return launched(hy::build_dense_pipe(a, L->family, padded_d(L->dk), n_seg, st), "prefill launch");
+    return launched(hy::build_dense_pipe(a, L->family, padded_d(L->dk), n_seg, st), "prefill launch", st);
 }
 
 int hypic_compose(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t max_list_len, const int32_t *d_list_off,
@@ -449,7 +464,7 @@ int hypic_pair_compact(const hypic_layout *L, int32_t n_slots, const float *d_T,
     if ((rc = injected("compact"))) return rc;
     return launched(hy::pair_compact(d_T, static_cast<hy::bf16 *>(d_Tc), d_Tscale, L->dk, (int64_t)n_slots * L->n_chains,
                                      reinterpret_cast<hipStream_t>(stream)),
-                    "pair compaction launch");
+                    "pair compaction launch", reinterpret_cast<hipStream_t>(stream));
 }
 
 int hypic_compose_compact(const hypic_layout *L, int32_t n_req, int32_t max_list_len, const int32_t *d_list_off,
@@ -492,7 +507,7 @@ int hypic_compose_compact(const hypic_layout *L, int32_t n_req, int32_t max_list
     a.state = d_state;
     a.o = d_o;
     a.prefix = d_prefix_states;
-    return launched(hy::compose_seq_compact(a, L->family, L->dk, n_req, st), "compact compose launch");
+    return launched(hy::compose_seq_compact(a, L->family, L->dk, n_req, st), "compact compose launch", st);
 }
 
 int hypic_rerotate(const hypic_layout *L, int32_t n_items, const int32_t *d_slot, const int64_t *d_offset,
@@ -530,7 +545,7 @@ int hypic_rerotate(const hypic_layout *L, int32_t n_items, const int32_t *d_slot
     a.S = d_S;
     a.T_out = d_T_out;
     a.S_out = d_S_out;
-    return launched(hy::rerotate(a, n_items, st), "re-rotation launch");
+    return launched(hy::rerotate(a, n_items, st), "re-rotation launch", st);
 }
 
 int hypic_conv_warmup(const hypic_layout *L, const hypic_tokens *raw, const float *d_taps, int32_t conv_k,
@@ -568,7 +583,7 @@ int hypic_conv_warmup(const hypic_layout *L, const hypic_tokens *raw, const floa
     a.q_out = d_q_out;
     a.k_out = d_k_out;
     a.v_out = d_v_out;
-    return launched(hy::conv_warmup(a, L->in_dtype == HYPIC_BF16, n_items, st), "conv warm-up launch");
+    return launched(hy::conv_warmup(a, L->in_dtype == HYPIC_BF16, n_items, st), "conv warm-up launch", st);
 }
 
 int hypic_seam_advance(const hypic_layout *L, const hypic_tokens *x, int32_t n_items, const int64_t *d_tok_begin,
@@ -599,7 +614,7 @@ int hypic_seam_advance(const hypic_layout *L, const hypic_tokens *x, int32_t n_i
     a.o = d_o;
     return launched(hy::seam_advance(a, L->family, L->in_dtype == HYPIC_BF16, padded_d(L->dk), n_items,
                                      reinterpret_cast<hipStream_t>(stream)),
-                    "seam advance launch");
+                    "seam advance launch", reinterpret_cast<hipStream_t>(stream));
 }
 
 const char *hypic_status_string(int status) {

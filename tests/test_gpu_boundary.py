@@ -1,8 +1,8 @@
 """GPU checks of the C ABI's options: the state after every entry
 (d_prefix_states), resuming a compose from a saved state in either mode, the
-HYPIC_VALIDATE read-back, and composition time that does not grow with
-segment length (codernav.top, section on linear layers: merging a cached
-segment is a constant-time step)."""
+HYPIC_VALIDATE read-back, the HYPIC_DEBUG synchronous launches, and
+composition time that does not grow with segment length (codernav.top,
+section on linear layers: merging a cached segment is a constant-time step)."""
 import os
 
 import numpy as np
@@ -202,3 +202,21 @@ def test_compose_time_independent_of_segment_length():
         torch.cuda.empty_cache()
     print("compose ms by segment length:", times, flush=True)
     assert 1 / 1.2 <= times[8200] / times[520] <= 1.2, times
+
+
+@pytest.mark.parametrize("fam,dtype,d,mode", [("gdn", "bf16", 128, "seq"), ("kda", "bf16", 64, "tree"),
+                                              ("gla", "bf16", 64, "tree")])
+def test_debug_synchronous_launches_change_nothing(fam, dtype, d, mode):
+    """HYPIC_DEBUG=1 synchronizes after every launch: pairs, states and seam
+    outputs are bitwise those of the asynchronous run, and every call still
+    returns success."""
+    wl = _wl(fam, dtype, d, [[70, 150, 64, 9, 90]], cid=91)
+    m = hy.TREE if mode == "tree" else hy.SEQ
+    ref = gpu_request(wl, mode=m)
+    os.environ["HYPIC_DEBUG"] = "1"
+    try:
+        dbg = gpu_request(wl, mode=m)
+    finally:
+        del os.environ["HYPIC_DEBUG"]
+    for key in ("T", "S", "state", "O"):
+        assert torch.equal(ref[key], dbg[key]), key
