@@ -245,8 +245,11 @@ k_build_diag(BuildArgs a) {
 // to LDS; each wave then adds K~^T V into its 32 columns of the slice state on
 // the matrix cores, through transpose reads.  A group's staging area is
 // double-buffered by chunk parity, so one barrier per chunk suffices and one
-// wave's staging overlaps another's products.  At the end the slice states
-// are combined through LDS; T = exp(sum of the segment's log-gates).
+// wave's staging overlaps another's products.  The groups meet only at the
+// end: each chunk's barrier is per group (an LDS arrival counter and a
+// bounded wait), so the groups drift apart and one group's staging issues
+// beside another's products.  At the end the slice states are combined
+// through LDS; T = exp(sum of the segment's log-gates).
 template <int D>
 struct SliceCfg {
     static constexpr int NW = D / 32;  // waves per slice group (one per 32 columns / 32 channels)
@@ -261,7 +264,9 @@ struct SliceCfg {
     static constexpr int GRP = al(gV + CS * LDK * 2);
     static constexpr int LDS_ = D + 4;  // fp32 row stride of the combine's S
     static constexpr int cS = 0, cTot = al(D * LDS_ * 4);
-    static constexpr int total = (2 * NG * GRP > cTot + NG * D * 4) ? 2 * NG * GRP : cTot + NG * D * 4;
+    static constexpr int main_ = (2 * NG * GRP > cTot + NG * D * 4) ? 2 * NG * GRP : cTot + NG * D * 4;
+    static constexpr int offCnt = al(main_);  // one arrival counter per slice group
+    static constexpr int total = offCnt + 16;
     static_assert(total <= 160 * 1024, "LDS budget");
 };
 
@@ -349,6 +354,9 @@ k_build_diag_slices(BuildArgs a) {
     float gsum[2] = {0.f, 0.f};  // summed log2-gates of this lane's tokens over the slice
 
     const int first = gi * per + per - 1;  // chunks run last to first
+    int *gcnt = reinterpret_cast<int *>(smem + Cfg::offCnt);
+    if (tid < NG) gcnt[tid] = 0;
+    __syncthreads();
     if (per > 0) fetch(first);
     for (int c = 0; c < per; ++c) {
         const int gc = first - c;
@@ -407,7 +415,15 @@ k_build_diag_slices(BuildArgs a) {
 #pragma unroll
             for (int e = 0; e < 2; ++e) Dd[e] = __shfl(W[e], r16);
         }
-        __syncthreads();
+        // the group's NW waves meet here (the other groups run on): every
+        // wave's staging of this chunk is in LDS before any of them reads it
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        if (lane == 0) atomicAdd(&gcnt[gi], 1);
+        {
+            const volatile int *vc = gcnt + gi;
+            for (int it = 0; it < (1 << 14) && *vc < NW * (c + 1); ++it) __builtin_amdgcn_s_sleep(1);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         fetch(gc - 1);
         // ---- carry: S_g += K~^T V for columns 32q .. 32q+31
         bf16x8 vb[2];
