@@ -712,45 +712,99 @@ __device__ void seam_chunk_bf16(f32x4 (&X)[D / 16][2], const SM &sm, int nt, flo
     s4v ah, al, mh, ml;
     split4v(arow, ah, al);
     split4v(mrow, mh, ml);
+    if constexpr (FAM == GDN) {
+        // GDN: the state update first (the caller's next step waits for it),
+        // the outputs after it.  That order spills fewer registers in the
+        // tree's block phase (102 per lane instead of 115 at d = 128; C4 tree
+        // 5.37-5.40 against 5.71-5.74 ms); for DeltaNet it spills more
+        // (4.46-4.50 against 4.31-4.33 ms), so DeltaNet keeps the outputs
+        // inside the loop.
+        s4v rh[2], rl[2];
 #pragma unroll
-    for (int n2 = 0; n2 < 2; ++n2) {
-        const int col = c0 + 16 * n2 + r16;
-        // Y rows 0-7 (lane groups 0, 1); zero in rows 8-15
-        f32x4 yv;
+        for (int n2 = 0; n2 < 2; ++n2) {
+            // Y rows 0-7 (lane groups 0, 1); zero in rows 8-15
+            f32x4 yv;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) yv[jj] = grp < 2 ? vv[n2][jj] - eg4[jj] * P[n2][jj] : 0.f;
-        s4v yh, yl;
-        split4v(yv, yh, yl);
-        f32x4 R = {0.f, 0.f, 0.f, 0.f};
-        R = mfma16(ah, yh, R);
-        R = mfma16(ah, yl, R);
-        R = mfma16(al, yh, R);
-        s4v rh, rl;
-        split4v(R, rh, rl);
-        // outputs, rows 8-15: o_t = e_t (Q S0)_t + (M R)_t
-        f32x4 O = {0.f, 0.f, 0.f, 0.f};
-        O = mfma16(mh, rh, O);
-        O = mfma16(mh, rl, O);
-        O = mfma16(ml, rh, O);
-        if (grp >= 2 && col < dk) {
+            for (int jj = 0; jj < 4; ++jj) yv[jj] = grp < 2 ? vv[n2][jj] - eg4[jj] * P[n2][jj] : 0.f;
+            s4v yh, yl;
+            split4v(yv, yh, yl);
+            f32x4 R = {0.f, 0.f, 0.f, 0.f};
+            R = mfma16(ah, yh, R);
+            R = mfma16(ah, yl, R);
+            R = mfma16(al, yh, R);
+            split4v(R, rh[n2], rl[n2]);
+            // S = lambda S0 + K^T diag(ec) R  (R rows 8-15 are zero)
+            f32x4 Rs = R;
+            if (grp < 2) {
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int t = 4 * (grp - 2) + jj;
-                if (t < nt) o_first[t * o_tok_stride + col] = eg4[jj] * P[n2][jj] + O[jj];
+                for (int jj = 0; jj < 4; ++jj) Rs[jj] *= ec4[jj];
+            }
+            s4v sh, sl;
+            split4v(Rs, sh, sl);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                f32x4 acc = X[rt][n2] * lam;
+                acc = mfma16(ktv[rt], sh, acc);
+                X[rt][n2] = mfma16(ktv[rt], sl, acc);
             }
         }
-        // S = lambda S0 + K^T diag(ec) R  (R rows 8-15 are zero)
-        f32x4 Rs = R;
-        if (grp < 2) {
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) Rs[jj] *= ec4[jj];
+        for (int n2 = 0; n2 < 2; ++n2) {
+            const int col = c0 + 16 * n2 + r16;
+            // outputs, rows 8-15: o_t = e_t (Q S0)_t + (M R)_t
+            f32x4 O = {0.f, 0.f, 0.f, 0.f};
+            O = mfma16(mh, rh[n2], O);
+            O = mfma16(mh, rl[n2], O);
+            O = mfma16(ml, rh[n2], O);
+            if (grp >= 2 && col < dk) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int t = 4 * (grp - 2) + jj;
+                    if (t < nt) o_first[t * o_tok_stride + col] = eg4[jj] * P[n2][jj] + O[jj];
+                }
+            }
         }
-        split4v(Rs, rh, rl);
+    } else {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            f32x4 acc = X[rt][n2] * lam;
-            acc = mfma16(ktv[rt], rh, acc);
-            X[rt][n2] = mfma16(ktv[rt], rl, acc);
+        for (int n2 = 0; n2 < 2; ++n2) {
+            const int col = c0 + 16 * n2 + r16;
+            // Y rows 0-7 (lane groups 0, 1); zero in rows 8-15
+            f32x4 yv;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) yv[jj] = grp < 2 ? vv[n2][jj] - eg4[jj] * P[n2][jj] : 0.f;
+            s4v yh, yl;
+            split4v(yv, yh, yl);
+            f32x4 R = {0.f, 0.f, 0.f, 0.f};
+            R = mfma16(ah, yh, R);
+            R = mfma16(ah, yl, R);
+            R = mfma16(al, yh, R);
+            s4v rh, rl;
+            split4v(R, rh, rl);
+            // outputs, rows 8-15: o_t = e_t (Q S0)_t + (M R)_t
+            f32x4 O = {0.f, 0.f, 0.f, 0.f};
+            O = mfma16(mh, rh, O);
+            O = mfma16(mh, rl, O);
+            O = mfma16(ml, rh, O);
+            if (grp >= 2 && col < dk) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int t = 4 * (grp - 2) + jj;
+                    if (t < nt) o_first[t * o_tok_stride + col] = eg4[jj] * P[n2][jj] + O[jj];
+                }
+            }
+            // S = lambda S0 + K^T diag(ec) R  (R rows 8-15 are zero)
+            f32x4 Rs = R;
+            if (grp < 2) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) Rs[jj] *= ec4[jj];
+            }
+            split4v(Rs, rh, rl);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                f32x4 acc = X[rt][n2] * lam;
+                acc = mfma16(ktv[rt], rh, acc);
+                X[rt][n2] = mfma16(ktv[rt], rl, acc);
+            }
         }
     }
 }
