@@ -287,6 +287,8 @@ int hypic_rerotate(const hypic_layout *L, int32_t n_items, const int32_t *d_slot
  *   d_q_out, d_k_out, d_v_out  [n_items][w][n_chains][dk] in the input dtype,
  *              ready to pass to hypic_compose / hypic_seam_advance as seam
  *              tokens (tok_stride n_chains * dk, window i at token i * w).
+ * raw q, k, v and the outputs 16-byte aligned, raw strides multiples of 16
+ * bytes (HYPIC_E_INVALID otherwise).
  */
 int hypic_conv_warmup(const hypic_layout *L, const hypic_tokens *raw, const float *d_taps, int32_t conv_k,
                       int32_t act, int32_t n_items, const int64_t *d_tok_begin, int32_t w, void *d_q_out,

@@ -562,6 +562,13 @@ int hypic_conv_warmup(const hypic_layout *L, const hypic_tokens *raw, const floa
     if (n_items == 0 || w == 0) return ok();
     if (!d_taps || !d_tok_begin || !d_q_out || !d_k_out || !d_v_out) return fail(HYPIC_E_INVALID, "NULL pointer");
     if ((int64_t)n_items * L->n_chains > 0x7fffffff) return fail(HYPIC_E_INVALID, "n_items * n_chains too large");
+    // (the kernel moves four channels per vector load and store)
+    const int es = esize(L->in_dtype);
+    if (((raw->tok_stride * es) & 15) || ((raw->chain_stride * es) & 15))
+        return fail(HYPIC_E_INVALID, "raw q/k/v strides must be multiples of 16 bytes");
+    if (!aligned16(raw->q) || !aligned16(raw->k) || !aligned16(raw->v) || !aligned16(d_q_out) ||
+        !aligned16(d_k_out) || !aligned16(d_v_out))
+        return fail(HYPIC_E_INVALID, "raw q/k/v and the outputs must be 16-byte aligned");
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (validate_on()) {
         std::vector<int64_t> tb;
@@ -574,6 +581,7 @@ int hypic_conv_warmup(const hypic_layout *L, const hypic_tokens *raw, const floa
     hy::ConvArgs a{};
     a.x = to_tok(raw);
     a.n_chains = L->n_chains;
+    a.n_items = n_items;
     a.dk = L->dk;
     a.w = w;
     a.K = conv_k;

@@ -91,6 +91,7 @@ struct RerotateArgs {
 struct ConvArgs {
     Tok x;  // raw (pre-convolution) q, k, v
     int n_chains;
+    int n_items;
     int dk;
     int w;
     int K;

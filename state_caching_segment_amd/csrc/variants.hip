@@ -19,6 +19,8 @@
 // as zero), optionally through SiLU.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -82,36 +84,73 @@ k_rerotate(RerotateArgs a) {
     }
 }
 
+// A thread takes CPT adjacent channels of one of q, k, v of one (item,
+// chain), so that each token row is one vector load and one vector store;
+// consecutive threads take consecutive channel groups, then tensors, chains
+// and items, and every thread of a workgroup has work.  The taps sit right-aligned in KMAX slots (zeros in front), so the
+// output for window token t is sum_m taps2[m] * b[t + m] over a buffer b
+// whose first KMAX - 1 entries are the tokens before the round: every index
+// is a compile-time constant for any conv_k.  Each round requests its TB
+// tokens before it uses any of them.
 template <typename TIN>
 __global__ void __launch_bounds__(VAR_THREADS)
 k_conv_warmup(ConvArgs a) {
-    constexpr int KMAX = 8;
-    const int item = blockIdx.x / a.n_chains, chain = blockIdx.x % a.n_chains;
-    const int64_t s0 = a.tok_begin[item];
-    for (int it = threadIdx.x; it < 3 * a.dk; it += VAR_THREADS) {
-        const int which = it / a.dk, c = it % a.dk;  // 0: q, 1: k, 2: v
+    constexpr int KMAX = 8, CPT = 4, TB = 8;
+    using V = typename std::conditional<std::is_same<TIN, float>::value, f32x4, bf16x4>::type;
+    const int K = a.K, nq = a.dk / CPT;
+    const int64_t ts = a.x.ts, ots = (int64_t)a.n_chains * a.dk;
+    const int64_t unit = (int64_t)blockIdx.x * VAR_THREADS + threadIdx.x;
+    if (unit < (int64_t)a.n_items * a.n_chains * 3 * nq) {
+        const int q4 = (int)(unit % nq), which = (int)(unit / nq % 3);  // 0: q, 1: k, 2: v
+        const int chain = (int)(unit / (3 * nq) % a.n_chains), item = (int)(unit / (3 * nq * a.n_chains));
+        const int c = q4 * CPT;
+        const int64_t s0 = a.tok_begin[item];
         const TIN *x = reinterpret_cast<const TIN *>(which == 0 ? a.x.q : which == 1 ? a.x.k : a.x.v) +
                        (int64_t)chain * a.x.cs + c;
         TIN *y = reinterpret_cast<TIN *>(which == 0 ? a.q_out : which == 1 ? a.k_out : a.v_out) +
                  ((int64_t)item * a.w * a.n_chains + chain) * a.dk + c;
-        const float *tp = a.taps + (((int64_t)which * a.n_chains + chain) * a.dk + c) * a.K;
-        float taps[KMAX], win[KMAX];
+        const float *tp = a.taps + (((int64_t)which * a.n_chains + chain) * a.dk + c) * K;
+        float taps2[CPT][KMAX];
 #pragma unroll
-        for (int j = 0; j < KMAX; ++j) {
-            taps[j] = j < a.K ? tp[j] : 0.f;
-            // window slot j holds token s0 - K + 1 + j (history first)
-            const int64_t u = s0 - a.K + 1 + j;
-            win[j] = (j < a.K - 1 && u >= 0) ? (float)x[u * a.x.ts] : 0.f;
+        for (int e = 0; e < CPT; ++e)
+#pragma unroll
+            for (int m = 0; m < KMAX; ++m) taps2[e][m] = m >= KMAX - K ? tp[e * K + m - (KMAX - K)] : 0.f;
+        float b[CPT][KMAX - 1 + TB];
+        // b[.][KMAX - 2 - i] = token s0 - 1 - i: the K - 1 tokens before the
+        // window (zero before token 0; older slots meet zero taps)
+#pragma unroll
+        for (int i = 0; i < KMAX - 1; ++i) {
+            const int64_t u = s0 - 1 - i;
+            V v{};
+            if (i < K - 1 && u >= 0) v = *reinterpret_cast<const V *>(x + u * ts);
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) b[e][KMAX - 2 - i] = (float)v[e];
         }
-        for (int t = 0; t < a.w; ++t) {
-            win[a.K - 1 < KMAX ? a.K - 1 : KMAX - 1] = (float)x[(s0 + t) * a.x.ts];
-            float z = 0.f;
+        for (int t0 = 0; t0 < a.w; t0 += TB) {
 #pragma unroll
-            for (int j = 0; j < KMAX; ++j) z += j < a.K ? taps[j] * win[j] : 0.f;
-            if (a.act == 1) z = z / (1.f + __expf(-z));
-            y[(int64_t)t * a.n_chains * a.dk] = (TIN)z;
+            for (int tt = 0; tt < TB; ++tt) {
+                V v{};
+                if (t0 + tt < a.w) v = *reinterpret_cast<const V *>(x + (s0 + t0 + tt) * ts);
 #pragma unroll
-            for (int j = 0; j + 1 < KMAX; ++j) win[j] = win[j + 1];
+                for (int e = 0; e < CPT; ++e) b[e][KMAX - 1 + tt] = (float)v[e];
+            }
+#pragma unroll
+            for (int tt = 0; tt < TB; ++tt) {
+                V out;
+#pragma unroll
+                for (int e = 0; e < CPT; ++e) {
+                    float z = 0.f;
+#pragma unroll
+                    for (int m = 0; m < KMAX; ++m) z += taps2[e][m] * b[e][tt + m];
+                    if (a.act == 1) z = z / (1.f + __expf(-z));
+                    out[e] = (TIN)z;
+                }
+                if (t0 + tt < a.w) *reinterpret_cast<V *>(y + (t0 + tt) * ots) = out;
+            }
+#pragma unroll
+            for (int e = 0; e < CPT; ++e)
+#pragma unroll
+                for (int i = 0; i < KMAX - 1; ++i) b[e][i] = b[e][TB + i];
         }
     }
 }
@@ -164,7 +203,8 @@ hipError_t rerotate(const RerotateArgs &a, int n_items, hipStream_t st) {
 }
 
 hipError_t conv_warmup(const ConvArgs &a, bool bf16_in, int n_items, hipStream_t st) {
-    const dim3 grid((unsigned)((int64_t)n_items * a.n_chains)), block(VAR_THREADS);
+    const int64_t units = (int64_t)n_items * a.n_chains * 3 * (a.dk / 4);
+    const dim3 grid((unsigned)((units + VAR_THREADS - 1) / VAR_THREADS)), block(VAR_THREADS);
     if (bf16_in)
         hipLaunchKernelGGL(k_conv_warmup<bf16>, grid, block, 0, st, a);
     else

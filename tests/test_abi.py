@@ -248,6 +248,9 @@ def test_variant_calls_validation():
     xq.q = None
     expect(-1, cw, L, xq, 16, 4, 1, 1, 8, 8, 16, 16, 16)      # raw q required
     cw(L, x, None, 4, 1, 0, None, 8, None, None, None)        # nothing to do
+    expect(-1, cw, L, _fake_tokens("gdn", "f32", align=4, cs=64), 16, 4, 1, 1, 8, 8, 16, 16, 16)  # raw misaligned
+    expect(-1, cw, L, _fake_tokens("gdn", "f32", cs=66), 16, 4, 1, 1, 8, 8, 16, 16, 16)  # raw stride
+    expect(-1, cw, L, x, 16, 4, 1, 1, 8, 8, 16, 24, 16)       # output misaligned
     os.environ["HYPIC_FAULT_INJECT"] = "rerotate"
     try:
         expect(-4, rr, L, 1, 8, 8, 10000.0, 16, 16, 16, 16)
