@@ -557,6 +557,12 @@ def main():
         cbc = cb - len(plan.pair_id) * C * d * d * 2.0   # T read in bf16: half its fp32 bytes
         out["compose_compact"] = {"ms": ms, "roofline": roof(cbc, cf, ms * 1e-3, "hbm") |
                                   {"kernel": "k_compose_lean (compact pairs)", "traffic": None}}
+        # the compaction itself: T read in fp32, T^ written in bf16, one scale per (slot, chain)
+        pc_ms = _median_ms(lambda: hy.hypic_pair_compact(lay.L, plan.n_slots, lay.T, Tc, sc, stream=stream),
+                           args.steps, stream)
+        pcb = plan.n_slots * C * (d * d * 6.0 + 4.0)
+        out["compose_compact"]["pair_compact"] = {"ms": pc_ms, "roofline": roof(pcb, 0.0, pc_ms * 1e-3, "hbm") |
+                                                  {"kernel": "k_pair_compact", "traffic": None}}
         del Tc, sc
     # variant patches at this shape: every cached pair re-rotated to its body's
     # absolute offset (rotary embeddings), and the seam windows' convolved

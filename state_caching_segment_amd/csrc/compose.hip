@@ -153,14 +153,15 @@ __device__ __forceinline__ float *seam_out(const TreeArgs &t, bool isS, int e, i
 }
 
 // One staged stage of nt seam tokens on the wave's columns.
-template <int D, int FAM, bool CHUNK, typename SM>
+template <int D, int FAM, bool CHUNK, typename SM, bool UPDATE_FIRST = false>
 __device__ __forceinline__ void seam_stage_run(f32x4 (&X)[D / 16][2], const SM &sm, int nt,
                                                float *o_first, const ComposeArgs &a, int c0, int dk,
                                                float (*nm)[SEAM_STAGE][9], bool v_zero) {
     if constexpr (CHUNK && FAM == KDA)
         seam_chunk_kda<D>(X, sm, nt, o_first, (int64_t)a.n_chains * dk, c0, dk, nm[0], nm[1], v_zero);
     else if constexpr (CHUNK)
-        seam_chunk_bf16<D, FAM>(X, sm, nt, o_first, (int64_t)a.n_chains * dk, c0, dk, nm[0], nm[1], v_zero);
+        seam_chunk_bf16<D, FAM, SM, UPDATE_FIRST>(X, sm, nt, o_first, (int64_t)a.n_chains * dk, c0, dk, nm[0],
+                                                  nm[1], v_zero);
     else
         seam_tokens<D, FAM>(X, sm, nt, o_first, (int64_t)a.n_chains * dk, c0, c0, v_zero, dk);
 }
@@ -328,7 +329,7 @@ k_compose_dense(TreeArgs t) {
                     __syncthreads();
                     seam_put<D, FAM, TIN>(sm, seam_pf, dk, a.w);
                     __syncthreads();
-                    seam_stage_run<D, FAM, CHUNK_SEAM>(X, sm, a.w, seam_out(t, isS, e, req, j0 + j, chain, 0, dk), a,
+                    seam_stage_run<D, FAM, CHUNK_SEAM, decltype(sm), TREE && FAM == GDN>(X, sm, a.w, seam_out(t, isS, e, req, j0 + j, chain, 0, dk), a,
                                                        c0, dk, seam_nm[wv], !isS);
                 }
             } else if (sb >= 0 && kda_one_stage) {
@@ -336,7 +337,7 @@ k_compose_dense(TreeArgs t) {
                     __syncthreads();
                     seam_put_kda<D, TIN, KNG>(sm, kda_pf, dk, a.w);
                     __syncthreads();
-                    seam_stage_run<D, FAM, CHUNK_SEAM>(X, sm, a.w, seam_out(t, isS, e, req, j0 + j, chain, 0, dk), a,
+                    seam_stage_run<D, FAM, CHUNK_SEAM, decltype(sm), TREE && FAM == GDN>(X, sm, a.w, seam_out(t, isS, e, req, j0 + j, chain, 0, dk), a,
                                                        c0, dk, seam_nm[wv], !isS);
                 }
             } else if (sb >= 0) {
@@ -348,7 +349,7 @@ k_compose_dense(TreeArgs t) {
                     else
                         stage_seam<D, FAM, TIN>(sm, a.x, chain, dk, sb + s0, nt);
                     __syncthreads();
-                    seam_stage_run<D, FAM, CHUNK_SEAM>(X, sm, nt, seam_out(t, isS, e, req, j0 + j, chain, s0, dk), a,
+                    seam_stage_run<D, FAM, CHUNK_SEAM, decltype(sm), TREE && FAM == GDN>(X, sm, nt, seam_out(t, isS, e, req, j0 + j, chain, s0, dk), a,
                                                        c0, dk, seam_nm[wv], !isS);
                 }
             }

@@ -583,7 +583,7 @@ __device__ __forceinline__ f32x4 mfma16(const s4v &a, const s4v &b, f32x4 c) {
 // a = beta = 1.  sNw, sMw: this wave's 8 x 9 fp32 scratch.  v_zero: the
 // tile's values are zero (the T half of a [T | S] pair), which makes the
 // read-out T^T q, the pulled-back query.
-template <int D, int FAM, typename SM>
+template <int D, int FAM, typename SM, bool UPDATE_FIRST = false>
 __device__ void seam_chunk_bf16(f32x4 (&X)[D / 16][2], const SM &sm, int nt, float *o_first,
                                 int64_t o_tok_stride, int c0, int dk, float (*sNw)[9], float (*sMw)[9],
                                 bool v_zero = false) {
@@ -712,12 +712,13 @@ __device__ void seam_chunk_bf16(f32x4 (&X)[D / 16][2], const SM &sm, int nt, flo
     s4v ah, al, mh, ml;
     split4v(arow, ah, al);
     split4v(mrow, mh, ml);
-    if constexpr (FAM == GDN) {
-        // GDN: the state update first (the caller's next step waits for it),
-        // the outputs after it.  That order spills fewer registers in the
-        // tree's block phase (102 per lane instead of 115 at d = 128; C4 tree
-        // 5.37-5.40 against 5.71-5.74 ms); for DeltaNet it spills more
-        // (4.46-4.50 against 4.31-4.33 ms), so DeltaNet keeps the outputs
+    if constexpr (UPDATE_FIRST) {
+        // The state update first (the caller's next step waits for it), the
+        // outputs after it.  The tree's block phase takes this order for GDN:
+        // it spills fewer registers there (102 per lane instead of 115 at
+        // d = 128; C4 tree 5.37-5.43 against 5.71-5.76 ms).  For DeltaNet's
+        // block phase it spills more (4.46-4.50 against 4.31-4.33 ms) and the
+        // lean compose runs as fast either way, so those keep the outputs
         // inside the loop.
         s4v rh[2], rl[2];
 #pragma unroll

@@ -166,10 +166,16 @@ k_pair_compact(const float *T, bf16 *Tc, float *scale, int dk) {
     const float *t = T + p * dk * dk;
     bf16 *tc = Tc + p * dk * dk;
     const int n4 = dk * dk / 4, tid = threadIdx.x;
+    // T is read once: each thread keeps its (at most 16) float4s for the
+    // conversion after the maximum is known
+    constexpr int MAXV = 128 * 128 / 4 / VAR_THREADS;
+    f32x4 v[MAXV];
     float mx = 0.f;
-    for (int i = tid; i < n4; i += VAR_THREADS) {
-        const f32x4 v = reinterpret_cast<const f32x4 *>(t)[i];
-        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+#pragma unroll
+    for (int r = 0; r < MAXV; ++r) {
+        const int i = tid + r * VAR_THREADS;
+        v[r] = i < n4 ? reinterpret_cast<const f32x4 *>(t)[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[r][0]), fabsf(v[r][1])), fmaxf(fabsf(v[r][2]), fabsf(v[r][3]))));
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
@@ -181,14 +187,15 @@ k_pair_compact(const float *T, bf16 *Tc, float *scale, int dk) {
     int e = 0;
     if (mx > 0.f && isfinite(mx)) frexpf(mx, &e);
     if (tid == 0) scale[p] = ldexpf(1.f, e);
-    for (int i = tid; i < n4; i += VAR_THREADS) {
-        const f32x4 v = reinterpret_cast<const f32x4 *>(t)[i];
+#pragma unroll
+    for (int r = 0; r < MAXV; ++r) {
+        const int i = tid + r * VAR_THREADS;
         bf16x4 h;
         // (ldexp, not a product with 2^-e: for a T in fp32's subnormal range
         // 2^-e itself overflows)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) h[k] = (bf16)ldexpf(v[k], -e);
-        reinterpret_cast<bf16x4 *>(tc)[i] = h;
+        for (int k = 0; k < 4; ++k) h[k] = (bf16)ldexpf(v[r][k], -e);
+        if (i < n4) reinterpret_cast<bf16x4 *>(tc)[i] = h;
     }
 }
 
