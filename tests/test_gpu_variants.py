@@ -55,15 +55,16 @@ def test_rerotate_matches_oracle(fam, d):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("K,act,w", [(4, 1, 8), (1, 0, 8), (8, 1, 8), (3, 0, 8), (4, 1, 5), (8, 0, 13), (3, 1, 20)])
-def test_conv_warmup_matches_oracle(dtype, K, act, w):
+@pytest.mark.parametrize("K,act,w,d", [(4, 1, 8, 64), (1, 0, 8, 64), (8, 1, 8, 64), (3, 0, 8, 64), (4, 1, 5, 64),
+                                       (8, 0, 13, 64), (3, 1, 20, 64), (8, 1, 13, 16), (2, 0, 9, 128)])
+def test_conv_warmup_matches_oracle(dtype, K, act, w, d):
     """Windows at token 0, 2 (history partly before the sequence) and inside
     it; every window's q, k, v against the oracle's convolution of the whole
     raw sequence at those positions.  Windows shorter than the kernel's
     eight-token round and spanning two and three rounds (the history carried
     from one round to the next)."""
     rng = np.random.default_rng(K)
-    n_tok, n_chains, d = 300, 3, 64
+    n_tok, n_chains = 300, 3
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
     raw = [torch.tensor(rng.normal(size=(n_tok, n_chains, d)), dtype=tdt, device="cuda") for _ in range(3)]
     taps = rng.normal(size=(3, n_chains, d, K)) / K
@@ -82,7 +83,7 @@ def test_conv_warmup_matches_oracle(dtype, K, act, w):
             for i, s in enumerate(starts):
                 got = outs[which][i, :, c].double().cpu().numpy()
                 worst = max(worst, oracle.rel_fro(got, full[s: s + w]))
-    print(f"conv warm-up {dtype} K={K} act={act} w={w}: {worst:.2e}", flush=True)
+    print(f"conv warm-up {dtype} K={K} act={act} w={w} d={d}: {worst:.2e}", flush=True)
     assert worst <= tol
 
 
