@@ -571,15 +571,19 @@ k_build_dense_pipe(BuildArgs a) {
 
     float *To = a.T + ((int64_t)seg * a.n_chains + chain) * dk * dk;
     float *So = a.S + ((int64_t)seg * a.n_chains + chain) * dk * dk;
+    // (row and column indices from a fresh lane index: shared with the
+    // identity start above, the compiler kept them across the chunk loop and
+    // spilled them in the prefill instantiation)
+    const int lf = lane_fresh(), fr16 = lf & 15, fgrp = lf >> 4;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const int row = 16 * rt + 4 * grp + jj;
+                const int row = 16 * rt + 4 * fgrp + jj;
                 const bool s_ = col0(nt) >= D;
-                const int col = col0(nt) + r16 - (s_ ? D : 0);
+                const int col = col0(nt) + fr16 - (s_ ? D : 0);
                 if (row < dk && col < dk) (s_ ? So : To)[row * dk + col] = X[rt][nt][jj];
             }
 }
