@@ -226,11 +226,14 @@ k_compose_dense(TreeArgs t) {
 
     f32x4 tpre[NV];
     f32x4 spre[RT][2];  // S_j rows: lane (4q + i, grp) holds row 4 grp + i, columns 4q .. 4q+3 of each tile
+    // (the loads, stores and products below take per-lane offsets from a
+    // fresh copy of the lane index, not from values held across the loop)
     auto t_load = [&](int j) {
         const float *Tp = a.T + (pid_at(j) * a.n_chains + chain) * a.t_elems;
+        const int lf = lane_fresh();
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int item = i * 64 + lane, row = wv * RPW + item / (D / 4), c4 = item % (D / 4);
+            const int item = i * 64 + lf, row = wv * RPW + item / (D / 4), c4 = item % (D / 4);
             if (D >= 64) {
                 tpre[i] = *reinterpret_cast<const f32x4 *>(Tp + row * D + 4 * c4);
             } else {
@@ -241,9 +244,10 @@ k_compose_dense(TreeArgs t) {
         }
     };
     auto t_put = [&](int buf) {
+        const int lf = lane_fresh();
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int item = i * 64 + lane, row = wv * RPW + item / (D / 4), c4 = item % (D / 4);
+            const int item = i * 64 + lf, row = wv * RPW + item / (D / 4), c4 = item % (D / 4);
             if (F32) {
                 *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(tsm[buf]) + row * LDT + 4 * c4) = tpre[i];
             } else {
@@ -264,7 +268,8 @@ k_compose_dense(TreeArgs t) {
     };
     auto s_load = [&](int j) {
         const float *Sp = a.S + (pid_at(j) * a.n_chains + chain) * dk * dk;
-        const int rw = 4 * grp + (r16 & 3), cl = c0 + 4 * (r16 >> 2);
+        const int lf = lane_fresh(), fr16 = lf & 15, fgrp = lf >> 4;
+        const int rw = 4 * fgrp + (fr16 & 3), cl = c0 + 4 * (fr16 >> 2);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -411,11 +416,12 @@ k_compose_dense(TreeArgs t) {
             if constexpr (KDA_PF)
                 if (kda_one_stage) seam_fetch_kda<D, TIN, KNG>(kda_pf, a.x, chain, dk, sb_at(jn), a.w);
             const bf16 *th = reinterpret_cast<const bf16 *>(tsm[j & 1]);
+            const int lp = lane_fresh(), pr16 = lp & 15, pgrp = lp >> 4;
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
-                    const int off = (16 * rt + r16) * LDT + 32 * kb + 8 * grp;
+                    const int off = (16 * rt + pr16) * LDT + 32 * kb + 8 * pgrp;
                     const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(th + off);
                     const bf16x8 al = *reinterpret_cast<const bf16x8 *>(th + D + off);
 #pragma unroll
