@@ -541,6 +541,20 @@ def main():
         out["prefill"] = {"ms": float(np.median(p_ms)), "ms_p10_p90": [float(np.percentile(p_ms, 10)),
                                                                         float(np.percentile(p_ms, 90))],
                           "tokens_per_s": v_tokens / tp, "ms_over_build": tp / tb, "roofline": rp}
+        if libs:
+            # the same prefill alternating over the libraries, step by step
+            pab = [[] for _ in libs]
+            for _ in range(args.steps):
+                for li, lib in enumerate(libs):
+                    hy.hypic.use(lib)
+                    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                    ev[0].record(stream)
+                    pf()
+                    ev[1].record(stream)
+                    torch.cuda.synchronize()
+                    pab[li].append(ev[0].elapsed_time(ev[1]))
+            hy.hypic.use(lib_a)
+            out["ab"]["prefill_ms"] = [float(np.median(x)) for x in pab]
         del pout, pT, pS
         torch.cuda.empty_cache()
     # compact pairs (bf16 T^ with a power-of-two scale): the same compose over them
