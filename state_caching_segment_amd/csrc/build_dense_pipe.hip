@@ -147,58 +147,37 @@ __device__ __forceinline__ void wave_lds_fence() {
 // so  O = diag(e^{Gamma_t}) Q S0 + diag(e^{Gamma_t - Gamma_c}) tril(Q K^T) R'
 // (tril inclusive): each S wave forms its 32 columns of O on the matrix cores
 // after its block solve, before the carry update.
-// One S wave's 32 output columns (c0 .. c0+31 of o) for the chunk of tokens
-// t0 .. t0 + min(L, 64) - 1, from the chunk-start state X (its S columns), the
-// solved R' (split, C layout per 16-row block) and the staged blocks of
-// tril(Q K^T); one 16-column half at a time, which bounds the registers held.
-template <int D, typename Cfg, int NT0>
-__device__ __forceinline__ void prefill_out(const f32x4 (&X)[D / 16][2], const s4 (&Rh)[4][2], const s4 (&Rl)[4][2],
+// One carry wave's 16 output columns (c0 + 16 .. c0 + 31 of o) for the chunk
+// of tokens t0 .. t0 + min(L, 64) - 1, from P = Q S0 on those columns (formed
+// beside Z = K X from the same split state), the solved R' (split, C layout
+// per 16-row block, tile 1) and the staged blocks of tril(Q K^T).
+template <int D, typename Cfg>
+__device__ __forceinline__ void prefill_out(const f32x4 (&P)[4], const s4 (&Rh)[4][2], const s4 (&Rl)[4][2],
                                             const char *buf, const BuildArgs &a, int64_t t0, int L, int chain, int c0) {
-    constexpr int KB = D / 32, LDK = Cfg::LDK, TILE = Cfg::TILE;
+    constexpr int TILE = Cfg::TILE;
+    constexpr int nt = 1;
     const int lane = lane_fresh(), r16 = lane & 15, grp = lane >> 4;
-    const bf16 *bQ = reinterpret_cast<const bf16 *>(buf + Cfg::bQ);
     const bf16 *bQK = reinterpret_cast<const bf16 *>(buf + Cfg::bQK);
     const float *bE = reinterpret_cast<const float *>(buf + Cfg::bE);
     bf16 *o = reinterpret_cast<bf16 *>(a.o) + (int64_t)chain * a.ocs + c0 + r16;
 #pragma unroll
-    for (int nt = NT0; nt < 2; ++nt) {
-        // P = Q S0 on this half's columns (the state split hi + lo; q exact in bf16)
-        f32x4 P[4];
+    for (int tb = 0; tb < 4; ++tb) {
+        f32x4 oi = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) P[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            bf16x8 xh, xl;
-            float xv[8];
-            acc_to_perm(X[2 * kb][nt], X[2 * kb + 1][nt], xv);
-            split8(xv, xh, xl);
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const bf16x8 qh = lds_perm(bQ, LDK, 16 * mt + r16, 32 * kb, grp);
-                P[mt] = mfma(qh, xh, P[mt]);
-                P[mt] = mfma(qh, xl, P[mt]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+        for (int ib = 0; ib <= tb; ++ib) {
+            s4 ch, cl;
+            tile_frag(bQK + (tb * (tb + 1) / 2 + ib) * TILE, r16, grp, ch, cl);
+            oi = mma16(ch, cl, Rh[ib][nt], Rl[ib][nt], oi);
         }
+        const f32x4 eo = *reinterpret_cast<const f32x4 *>(bE + CH + 16 * tb + 4 * grp);
+        const f32x4 ei = *reinterpret_cast<const f32x4 *>(bE + 2 * CH + 16 * tb + 4 * grp);
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            f32x4 oi = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ib = 0; ib <= tb; ++ib) {
-                s4 ch, cl;
-                tile_frag(bQK + (tb * (tb + 1) / 2 + ib) * TILE, r16, grp, ch, cl);
-                oi = mma16(ch, cl, Rh[ib][nt], Rl[ib][nt], oi);
-            }
-            const f32x4 eo = *reinterpret_cast<const f32x4 *>(bE + CH + 16 * tb + 4 * grp);
-            const f32x4 ei = *reinterpret_cast<const f32x4 *>(bE + 2 * CH + 16 * tb + 4 * grp);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int t = 16 * tb + 4 * grp + jj;
-                const float v = eo[jj] * P[tb][jj] + ei[jj] * oi[jj];
-                if (t < L && c0 + 16 * nt + r16 < a.dk) o[(t0 + t) * a.ots + 16 * nt] = (bf16)v;
-            }
-            __builtin_amdgcn_sched_barrier(0);
+        for (int jj = 0; jj < 4; ++jj) {
+            const int t = 16 * tb + 4 * grp + jj;
+            const float v = eo[jj] * P[tb][jj] + ei[jj] * oi[jj];
+            if (t < L && c0 + 16 * nt + r16 < a.dk) o[(t0 + t) * a.ots + 16 * nt] = (bf16)v;
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -470,7 +449,11 @@ k_build_dense_pipe(BuildArgs a) {
         const bf16 *bA = reinterpret_cast<const bf16 *>(buf + Cfg::bA);
         const bf16 *bM = reinterpret_cast<const bf16 *>(buf + Cfg::bM);
         const float lam = FAM == GDN ? *reinterpret_cast<const float *>(buf + Cfg::bLam) : 1.f;
-        // Z = K X
+        // Z = K X (and, for the prefill, QS = Q S0 on the S tile)
+        const bf16 *bQ = reinterpret_cast<const bf16 *>(buf + Cfg::bQ);
+        f32x4 QS[PF ? 4 : 1];
+#pragma unroll
+        for (int mt = 0; mt < (PF ? 4 : 1); ++mt) QS[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         f32x4 Z[4][2];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
@@ -492,6 +475,12 @@ k_build_dense_pipe(BuildArgs a) {
                 for (int nt = 0; nt < 2; ++nt) {
                     Z[mt][nt] = mfma(kh, xh[nt], Z[mt][nt]);
                     Z[mt][nt] = mfma(kh, xl[nt], Z[mt][nt]);
+                }
+                if constexpr (PF) {
+                    // Q S0 on the S tile, from the same split state
+                    const bf16x8 qh = lds_perm(bQ, LDK, 16 * mt + r16, 32 * kb, grp);
+                    QS[mt] = mfma(qh, xh[1], QS[mt]);
+                    QS[mt] = mfma(qh, xl[1], QS[mt]);
                 }
             }
         }
@@ -538,7 +527,7 @@ k_build_dense_pipe(BuildArgs a) {
             for (int nt = 0; nt < 2; ++nt) split4(r[nt], Rh[b][nt], Rl[b][nt]);
         }
         if constexpr (PF) {
-            prefill_out<D, Cfg, 1>(X, Rh, Rl, buf, a, b0 + (int64_t)c * CH, (int)(n - (int64_t)c * CH), chain,
+            prefill_out<D, Cfg>(QS, Rh, Rl, buf, a, b0 + (int64_t)c * CH, (int)(n - (int64_t)c * CH), chain,
                                    16 * wv - 16);
         }
         // X = lambda X + K^T R'
