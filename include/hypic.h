@@ -169,7 +169,9 @@ int hypic_segment_build(const hypic_layout *L, const hypic_tokens *x, int32_t n_
  * required.  Implemented for DeltaNet and GDN with bf16 inputs
  * (HYPIC_E_UNSUPPORTED otherwise).  Every chunk of 64 tokens must keep its
  * total log-decay above about -80 (the chunk form scales the solved rows by
- * the chunk's decay).  d_out must not overlap the inputs or the pair.
+ * the chunk's decay).  d_out must not overlap the inputs or the pair; it is
+ * 8-byte aligned with strides that are multiples of 4 elements
+ * (HYPIC_E_INVALID otherwise).
  */
 int hypic_segment_prefill(const hypic_layout *L, const hypic_tokens *x, int32_t n_seg,
                           const int64_t *d_seg_begin, const int64_t *d_seg_end, int64_t max_seg_len,

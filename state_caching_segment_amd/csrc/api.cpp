@@ -414,6 +414,9 @@ int hypic_segment_prefill(const hypic_layout *L, const hypic_tokens *x, int32_t 
     if (n_seg == 0) return ok();
     if (!d_seg_begin || !d_seg_end || !d_T || !d_S || !d_out)
         return fail(HYPIC_E_INVALID, "NULL segment or output pointer");
+    // (the outputs leave as four-element row pieces)
+    if ((out_tok_stride & 3) || (out_chain_stride & 3) || (reinterpret_cast<uintptr_t>(d_out) & 7))
+        return fail(HYPIC_E_INVALID, "prefill output: strides must be multiples of 4 elements, d_out 8-byte aligned");
     if ((int64_t)n_seg * L->n_chains > 0x7fffffff) return fail(HYPIC_E_INVALID, "n_seg * n_chains too large");
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (validate_on() && (rc = validate_segments(n_seg, d_seg_begin, d_seg_end, max_seg_len, st))) return rc;

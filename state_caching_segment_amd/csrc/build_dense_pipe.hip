@@ -150,16 +150,19 @@ __device__ __forceinline__ void wave_lds_fence() {
 // One carry wave's 16 output columns (c0 + 16 .. c0 + 31 of o) for the chunk
 // of tokens t0 .. t0 + min(L, 64) - 1, from P = Q S0 on those columns (formed
 // beside Z = K X from the same split state), the solved R' (split, C layout
-// per 16-row block, tile 1) and the staged blocks of tril(Q K^T).
+// per 16-row block, tile 1) and the staged blocks of tril(Q K^T).  The bf16
+// outputs are staged transposed in this wave's own 16 rows of the chunk's V^T
+// (read only by this wave, in its Y step) and leave as 8-byte row pieces:
+// four stores per lane instead of sixteen 2-byte ones.
 template <int D, typename Cfg>
 __device__ __forceinline__ void prefill_out(const f32x4 (&P)[4], const s4 (&Rh)[4][2], const s4 (&Rl)[4][2],
                                             const char *buf, const BuildArgs &a, int64_t t0, int L, int chain, int c0) {
-    constexpr int TILE = Cfg::TILE;
+    constexpr int TILE = Cfg::TILE, LDVB = Cfg::LDVB;
     constexpr int nt = 1;
     const int lane = lane_fresh(), r16 = lane & 15, grp = lane >> 4;
     const bf16 *bQK = reinterpret_cast<const bf16 *>(buf + Cfg::bQK);
     const float *bE = reinterpret_cast<const float *>(buf + Cfg::bE);
-    bf16 *o = reinterpret_cast<bf16 *>(a.o) + (int64_t)chain * a.ocs + c0 + r16;
+    bf16 *stg = const_cast<bf16 *>(reinterpret_cast<const bf16 *>(buf + Cfg::bV)) + (c0 + 16) * LDVB;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
         f32x4 oi = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -171,13 +174,22 @@ __device__ __forceinline__ void prefill_out(const f32x4 (&P)[4], const s4 (&Rh)[
         }
         const f32x4 eo = *reinterpret_cast<const f32x4 *>(bE + CH + 16 * tb + 4 * grp);
         const f32x4 ei = *reinterpret_cast<const f32x4 *>(bE + 2 * CH + 16 * tb + 4 * grp);
+        bf16x4 ov;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int t = 16 * tb + 4 * grp + jj;
-            const float v = eo[jj] * P[tb][jj] + ei[jj] * oi[jj];
-            if (t < L && c0 + 16 * nt + r16 < a.dk) o[(t0 + t) * a.ots + 16 * nt] = (bf16)v;
-        }
+        for (int jj = 0; jj < 4; ++jj) ov[jj] = (bf16)(eo[jj] * P[tb][jj] + ei[jj] * oi[jj]);
+        // column r16, tokens 16 tb + 4 grp .. + 3
+        *reinterpret_cast<bf16x4 *>(stg + r16 * LDVB + 16 * tb + 4 * grp) = ov;
         __builtin_amdgcn_sched_barrier(0);
+    }
+    wave_lds_fence();
+    // lane group g takes columns 4 g .. 4 g + 3 of token 16 blk + r16
+    bf16 *o = reinterpret_cast<bf16 *>(a.o) + (int64_t)chain * a.ocs + c0 + 16 + 4 * grp;
+    const bool col_ok = c0 + 16 + 4 * grp < a.dk;
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+        const bf16x4 w = lds_tr4(stg, LDVB, 4 * grp, 16 * blk, r16);
+        const int t = 16 * blk + r16;
+        if (t < L && col_ok) *reinterpret_cast<bf16x4 *>(o + (t0 + t) * a.ots) = w;
     }
 }
 

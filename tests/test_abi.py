@@ -225,6 +225,21 @@ def test_request_plan_longest_first():
         request_plan(reqs, 8, slot_order="random")
 
 
+def test_prefill_output_layout_validation():
+    """hypic_segment_prefill refuses an output it cannot write in four-element
+    row pieces (strides not multiples of 4 elements, or d_out not 8-byte
+    aligned), before any HIP call."""
+    L = hy.layout("gdn", "bf16", 4, 128)
+    x = _fake_tokens("gdn", "bf16")
+    fn = hy.load().hypic_segment_prefill
+    base = 1 << 21
+    args = lambda out, ts, cs: (ctypes.byref(L), ctypes.byref(x), 1, ctypes.c_void_p(base), ctypes.c_void_p(base),
+                                64, ctypes.c_void_p(base), ctypes.c_void_p(base), ctypes.c_void_p(out), ts, cs, None)
+    assert fn(*args(base + 4, 512, 128)) == -1    # d_out misaligned
+    assert fn(*args(base, 514, 128)) == -1        # token stride
+    assert fn(*args(base, 512, 130)) == -1        # chain stride
+
+
 def test_variant_calls_validation():
     """hypic_rerotate and hypic_conv_warmup reject bad arguments before any
     HIP call; families whose per-channel decay does not commute with the
