@@ -467,7 +467,9 @@ k_compose_dense(TreeArgs t) {
 //            cores);
 //   product: the state becomes the split B operand, S_j is requested, the
 //            accumulators run T_j S from the LDS copy and then take + S_j
-//            (the loads have the product's length to arrive);
+//            (the compiler issues the S_j loads at the end of the product,
+//            which keeps the product within 256 registers; they arrive with
+//            T_{j+1}'s, and the add is folded into the next entry's start);
 //   staging: once every wave is past the product, the next window and
 //            T_{j+1} are requested and written into LDS (the wait for them is
 //            the other workgroup's time on the compute unit).
