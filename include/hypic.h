@@ -210,6 +210,8 @@ int hypic_segment_prefill(const hypic_layout *L, const hypic_tokens *x, int32_t 
  * workspace of hypic_workspace_bytes(L, HYPIC_OP_COMPOSE_TREE, n_req,
  * max_list_len, w) bytes (HYPIC_E_WORKSPACE if missing or smaller).  HYPIC_SEQ
  * needs none.  max_list_len must bound every request's entry count.
+ * Alignment: d_T and d_S 16-byte, d_state, d_o and d_prefix_states 4-byte
+ * (HYPIC_E_INVALID otherwise).
  */
 int hypic_compose(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t max_list_len,
                   const int32_t *d_list_off, const int32_t *d_pair_id, int64_t n_slots,
@@ -308,7 +310,8 @@ int hypic_conv_warmup(const hypic_layout *L, const hypic_tokens *raw, const floa
  * hypic_compose over compact pairs (T^ read in bf16: 64 + 32 KiB per pair and
  * chain at d = 128 instead of 128 KiB); DeltaNet and GDN with bf16 inputs,
  * dk >= 64.  T^'s rounding (relative 2^-8 at most per element) enters each step's
- * T S, so its error is that of bf16 T, not of the fp32 pair.
+ * T S, so its error is that of bf16 T, not of the fp32 pair.  Alignment:
+ * d_Tc 8-byte, d_S 16-byte, d_state, d_o and d_prefix_states 4-byte.
  */
 int hypic_pair_compact(const hypic_layout *L, int32_t n_slots, const float *d_T, void *d_Tc, float *d_Tscale,
                        void *stream);

@@ -35,6 +35,7 @@ int ok() {
 constexpr int64_t kMaxTokStride = int64_t(1) << 24;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 int esize(int dtype) { return dtype == HYPIC_BF16 ? 2 : 4; }
 
@@ -342,6 +343,10 @@ int compose_call(const hypic_layout *L, int32_t mode, int32_t n_req, int32_t max
         if ((rc = check_tokens(L, seam, true))) return rc;
         if (!d_seam_begin || !d_o) return fail(HYPIC_E_INVALID, "seams need d_seam_begin and d_o");
     }
+    // (pairs are read 16 bytes at a time; states and outputs are fp32)
+    if ((max_list_len > 0 && (!aligned16(d_T) || !aligned16(d_S))) || !aligned4(d_state) ||
+        (has_seam && !aligned4(d_o)) || !aligned4(d_prefix_states))
+        return fail(HYPIC_E_INVALID, "pairs must be 16-byte aligned, states and outputs 4-byte aligned");
     hy::ComposeArgs a{};
     a.x = has_seam ? to_tok(seam) : hy::Tok{};
     a.n_chains = L->n_chains;
@@ -489,6 +494,9 @@ int hypic_compose_compact(const hypic_layout *L, int32_t n_req, int32_t max_list
         if ((rc = check_tokens(L, seam, true))) return rc;
         if (!d_seam_begin || !d_o) return fail(HYPIC_E_INVALID, "seams need d_seam_begin and d_o");
     }
+    if ((max_list_len > 0 && ((reinterpret_cast<uintptr_t>(d_Tc) & 7u) || !aligned16(d_S))) || !aligned4(d_state) ||
+        (has_seam && !aligned4(d_o)) || !aligned4(d_prefix_states))
+        return fail(HYPIC_E_INVALID, "compact T must be 8-byte, S 16-byte, states and outputs 4-byte aligned");
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (validate_on() &&
         (rc = validate_lists(n_req, max_list_len, d_list_off, d_pair_id, n_slots, has_seam ? d_seam_begin : nullptr, st)))

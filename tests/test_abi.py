@@ -52,6 +52,11 @@ def _fake_tokens(family, dtype="bf16", align=0, ts=None, cs=128):
     return t
 
 
+# a stand-in device pointer (never dereferenced: every call here fails or
+# returns before a launch), aligned as the calls require
+P = 256
+
+
 def expect(status, fn, *args):
     with pytest.raises(hy.HypicError) as e:
         fn(*args)
@@ -90,15 +95,20 @@ def test_compose_and_seam_validation():
     L = hy.layout("gdn", "bf16", 4, 64)
     x = _fake_tokens("gdn", cs=64)
     c = hy.hypic_compose
-    expect(-1, c, L, 5, 1, 2, 8, 8, 2, 8, 8, None, None, 0, 8, None)           # mode
-    expect(-1, c, L, hy.SEQ, 1, 2, 8, 8, 2, 8, 8, x, 8, -1, 8, 8)              # w < 0
-    expect(-1, c, L, hy.SEQ, 1, 2, None, 8, 2, 8, 8, None, None, 0, 8, None)   # NULL list
-    expect(-1, c, L, hy.SEQ, 1, 2, 8, 8, 2, 8, 8, x, None, 8, 8, 8)            # seams without begin
-    expect(-1, c, L, hy.SEQ, 1, 2, 8, 8, 2, 8, 8, x, 8, 8, 8, None)            # seams without outputs
+    expect(-1, c, L, 5, 1, 2, P, P, 2, P, P, None, None, 0, P, None)           # mode
+    expect(-1, c, L, hy.SEQ, 1, 2, P, P, 2, P, P, x, P, -1, P, P)              # w < 0
+    expect(-1, c, L, hy.SEQ, 1, 2, None, P, 2, P, P, None, None, 0, P, None)   # NULL list
+    expect(-1, c, L, hy.SEQ, 1, 2, P, P, 2, P, P, x, None, 8, P, P)            # seams without begin
+    expect(-1, c, L, hy.SEQ, 1, 2, P, P, 2, P, P, x, P, 8, P, None)            # seams without outputs
     xq = _fake_tokens("gdn", cs=64)
     xq.q = None
-    expect(-1, c, L, hy.SEQ, 1, 2, 8, 8, 2, 8, 8, xq, 8, 8, 8, 8)              # seams need q
-    expect(-3, c, L, hy.TREE, 1, 2, 8, 8, 2, 8, 8, None, None, 0, 8, None)     # tree needs a workspace
+    expect(-1, c, L, hy.SEQ, 1, 2, P, P, 2, P, P, xq, P, 8, P, P)              # seams need q
+    expect(-3, c, L, hy.TREE, 1, 2, P, P, 2, P, P, None, None, 0, P, None)     # tree needs a workspace
+    # pairs 16-byte, states and outputs 4-byte aligned
+    expect(-1, c, L, hy.SEQ, 1, 2, P, P, 2, P + 8, P, None, None, 0, P, None)  # T
+    expect(-1, c, L, hy.SEQ, 1, 2, P, P, 2, P, P + 8, None, None, 0, P, None)  # S
+    expect(-1, c, L, hy.SEQ, 1, 2, P, P, 2, P, P, None, None, 0, P + 2, None)  # state
+    expect(-1, c, L, hy.SEQ, 1, 2, P, P, 2, P, P, x, P, 8, P, P + 2)           # outputs
     c(L, hy.SEQ, 0, 0, None, None, 0, None, None, None, None, 0, None, None)   # empty: OK
     s = hy.hypic_seam_advance
     expect(-1, s, L, x, 2, None, 8, 8, 8)
@@ -112,11 +122,11 @@ def test_token_stride_bound():
     L = hy.layout("gdn", "f32", 4, 64)
     big = (1 << 24) + 64
     expect(-2, hy.hypic_segment_build, L, _fake_tokens("gdn", "f32", ts=big, cs=64), 1, 8, 8, 10, 8, 8)
-    expect(-2, hy.hypic_compose, L, hy.SEQ, 1, 2, 8, 8, 2, 8, 8, _fake_tokens("gdn", "f32", ts=big, cs=64), 8, 8, 8, 8)
+    expect(-2, hy.hypic_compose, L, hy.SEQ, 1, 2, P, P, 2, P, P, _fake_tokens("gdn", "f32", ts=big, cs=64), P, 8, P, P)
     expect(-2, hy.hypic_seam_advance, L, _fake_tokens("gdn", "f32", ts=big, cs=64), 2, 8, 8, 8, 8)
     xg = _fake_tokens("gdn", "f32", cs=64)
     xg.g_tok_stride = big
-    expect(-2, hy.hypic_compose, L, hy.SEQ, 1, 2, 8, 8, 2, 8, 8, xg, 8, 8, 8, 8)
+    expect(-2, hy.hypic_compose, L, hy.SEQ, 1, 2, P, P, 2, P, P, xg, P, 8, P, P)
     xb = _fake_tokens("gdn", "f32", cs=64)
     xb.b_tok_stride = big
     expect(-2, hy.hypic_seam_advance, L, xb, 2, 8, 8, 8, 8)
@@ -124,7 +134,7 @@ def test_token_stride_bound():
     ok = _fake_tokens("gdn", "f32", ts=1 << 24, cs=64)
     os.environ["HYPIC_FAULT_INJECT"] = "all"
     try:
-        expect(-4, hy.hypic_compose, L, hy.SEQ, 1, 2, 8, 8, 2, 8, 8, ok, 8, 8, 8, 8)
+        expect(-4, hy.hypic_compose, L, hy.SEQ, 1, 2, P, P, 2, P, P, ok, P, 8, P, P)
     finally:
         del os.environ["HYPIC_FAULT_INJECT"]
 
@@ -143,16 +153,16 @@ def test_fault_injection():
             expect(-1, hy.hypic_segment_build, L, x, -1, 8, 8, 10, 8, 8)   # validation first
         for val in ("1", "compose"):
             os.environ["HYPIC_FAULT_INJECT"] = val
-            expect(-4, hy.hypic_compose, L, hy.SEQ, 1, 2, 8, 8, 2, 8, 8, x, 8, 8, 8, 8)
+            expect(-4, hy.hypic_compose, L, hy.SEQ, 1, 2, P, P, 2, P, P, x, P, 8, P, P)
             # tree mode: the workspace check comes before the injected fault
-            expect(-3, hy.hypic_compose, L, hy.TREE, 1, 2, 8, 8, 2, 8, 8, None, None, 0, 8, None)
-            expect(-4, hy.hypic_compose, L, hy.TREE, 1, 2, 8, 8, 2, 8, 8, None, None, 0, 8, None, None, 8,
+            expect(-3, hy.hypic_compose, L, hy.TREE, 1, 2, P, P, 2, P, P, None, None, 0, P, None)
+            expect(-4, hy.hypic_compose, L, hy.TREE, 1, 2, P, P, 2, P, P, None, None, 0, P, None, None, P,
                    1 << 30)
         for val in ("1", "seam"):
             os.environ["HYPIC_FAULT_INJECT"] = val
             expect(-4, hy.hypic_seam_advance, L, x, 2, 8, 8, 8, 8)
         os.environ["HYPIC_FAULT_INJECT"] = "seam"   # other calls unaffected: they reach their own checks
-        expect(-1, hy.hypic_compose, L, hy.SEQ, 1, 2, 8, 8, 2, 8, 8, x, 8, -1, 8, 8)
+        expect(-1, hy.hypic_compose, L, hy.SEQ, 1, 2, P, P, 2, P, P, x, P, -1, P, P)
         os.environ["HYPIC_FAULT_INJECT"] = "0"
         expect(-1, hy.hypic_seam_advance, L, x, 2, 8, -3, 8, 8)
     finally:

@@ -74,5 +74,7 @@ def test_noalloc_rejects_oversize_before_any_launch():
     need = hy.hypic_workspace_bytes(L, hy.OP_COMPOSE_TREE, 16, 128, 8)
     assert need > hy.NOALLOC_WORKSPACE_BYTES
     with pytest.raises(hy.HypicError) as e:
-        hy.hypic_compose_tree_noalloc(L, 16, 128, 8, 8, 10, 8, 8, None, None, 0, 8, None)
+        # (device pointers are never dereferenced here; they only need the
+        # alignment the call checks first)
+        hy.hypic_compose_tree_noalloc(L, 16, 128, 16, 16, 10, 16, 16, None, None, 0, 16, None)
     assert e.value.status == -3 and str(hy.NOALLOC_WORKSPACE_BYTES) in str(e.value)
