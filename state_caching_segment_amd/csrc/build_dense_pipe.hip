@@ -439,11 +439,18 @@ k_build_dense_pipe(BuildArgs a) {
     }
 
     const int lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
-    // Columns of [T | S] per wave.  Plain build: wave wv holds columns
-    // 32 wv .. 32 wv + 31.  Prefill: tile 0 holds T columns 16 wv .. 16 wv + 15
+    // Columns of [T | S] per wave.  Plain build: carry slot p holds columns
+    // 32 p .. 32 p + 31 (T: p < d/32).  Wave i of the workgroup runs on SIMD
+    // i % 4, so the factor waves (NC, NC + 1) share SIMDs 0 and 1 with carry
+    // waves; at d = 128 those are given T slots, whose waves finish their
+    // chunk earlier than the S waves (E V), and the S waves take SIMDs 2 and
+    // 3: 12.72 against 12.85 ms at C4 in the same calls (S waves beside the
+    // factor waves instead, 12.84).  At d <= 64 the T waves are on SIMDs 0
+    // and 1 as they stand.  Prefill: tile 0 holds T columns 16 wv .. 16 wv + 15
     // and tile 1 the same columns of S, so that every carry wave writes the
     // outputs of 16 columns (the outputs cost as much as the carry of S).
-    const int cbase = wv * 32;
+    const int slot = PF || NC != 8 ? wv : (wv & 1) + 2 * (wv >> 2) + 4 * ((wv >> 1) & 1);
+    const int cbase = slot * 32;
     const bool isS = cbase >= D;
     auto col0 = [&](int nt) { return PF ? (nt ? D : 0) + 16 * wv : cbase + 16 * nt; };
     f32x4 X[RT][2];
