@@ -444,9 +444,10 @@ k_build_dense_pipe(BuildArgs a) {
     // i % 4, so the factor waves (NC, NC + 1) share SIMDs 0 and 1 with carry
     // waves; at d = 128 those are given T slots, whose waves finish their
     // chunk earlier than the S waves (E V), and the S waves take SIMDs 2 and
-    // 3: 12.72 against 12.85 ms at C4 in the same calls (S waves beside the
-    // factor waves instead, 12.84).  At d <= 64 the T waves are on SIMDs 0
-    // and 1 as they stand.  Prefill: tile 0 holds T columns 16 wv .. 16 wv + 15
+    // 3: 12.72 against 12.85 ms for 960 GDN chains of a 32k-token request in
+    // the same calls (S waves beside the factor waves instead, 12.84).  At
+    // d <= 64 the T waves are on SIMDs 0 and 1 as they stand.  Prefill: tile
+    // 0 holds T columns 16 wv .. 16 wv + 15
     // and tile 1 the same columns of S, so that every carry wave writes the
     // outputs of 16 columns (the outputs cost as much as the carry of S).
     const int slot = PF || NC != 8 ? wv : (wv & 1) + 2 * (wv >> 2) + 4 * ((wv >> 1) & 1);

@@ -643,9 +643,10 @@ k_compose_lean(TreeArgs targ) {
                 // (staged during the previous staging phase)
                 seam_chunk_bf16<D, FAM>(X, sm, a.w, o_first, (int64_t)a.n_chains * dk, c0, dk, seam_nm[wv][0],
                                         seam_nm[wv][1]);
-                // the window's output stores complete before S_j is requested:
-                // 1.321-1.323 against 1.338-1.343 ms on C4 in the same call
-                // (the memory counter is counted in issue order)
+                // the window's output stores complete before S_j is requested
+                // (the memory counter is counted in issue order): 1.321-1.323
+                // against 1.338-1.343 ms on 960 GDN chains (d = 128, 48
+                // entries) in the same call
                 __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
             } else if (sb >= 0) {
                 for (int s0 = 0; s0 < a.w; s0 += SEAM_STAGE) {

@@ -713,14 +713,15 @@ __device__ void seam_chunk_bf16(f32x4 (&X)[D / 16][2], const SM &sm, int nt, flo
     split4v(arow, ah, al);
     split4v(mrow, mh, ml);
     // (the outputs are stored non-temporal: nothing here reads them again;
-    // the C4 lean compose takes 1.312-1.315 ms against 1.318-1.328 with plain
-    // stores in the same calls)
+    // the lean compose over 960 GDN chains, d = 128, 48 entries, takes
+    // 1.312-1.315 ms against 1.318-1.328 with plain stores in the same calls)
     if constexpr (UPDATE_FIRST) {
         // The state update first (the caller's next step waits for it), the
         // outputs after it.  The tree's block phase takes this order for GDN:
         // it spills fewer registers there (102 per lane instead of 115 at
-        // d = 128; C4 tree 5.37-5.43 against 5.71-5.76 ms).  For DeltaNet's
-        // block phase it spills more (4.46-4.50 against 4.31-4.33 ms) and the
+        // d = 128; tree over 960 GDN chains 5.37-5.43 against 5.71-5.76 ms).
+        // For DeltaNet's block phase it spills more (4.46-4.50 against
+        // 4.31-4.33 ms) and the
         // lean compose runs as fast either way, so those keep the outputs
         // inside the loop.
         s4v rh[2], rl[2];

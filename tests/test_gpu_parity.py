@@ -5,7 +5,7 @@ Tolerance: relative Frobenius error per object <= 1e-4 for fp32 inputs and
 <= 5e-3 for bf16 inputs with fp32 state.  Sizes span several 64-token chunks
 and ragged tails (lengths 9, 64+8, 65+8, 130, 513 ...), every family, d in
 {16, 32, 64, 128}; the full-size GDN request (960 chains, 32768 tokens), the
-full C3 GLA request and a full KDA layer (16 requests of 100000 tokens, tree
+full GLA request (16 chains, 32 segments of 512-2048 tokens) and a full KDA layer (16 requests of 100000 tokens, tree
 compose) are checked on samples of chains and requests.
 """
 import numpy as np
@@ -132,7 +132,8 @@ def test_retnet_c2_closed_form_and_naive_addition():
 
 
 def test_gla_c3_sampled():
-    """The full C3 request, sequential compose and the tree scan bench.py times."""
+    """The full GLA request (16 chains, d = 128, 32 segments of 512-2048
+    tokens), sequential compose and the tree scan bench.py times."""
     wl = workloads.config("c3", device="cuda")
     check(wl, chains=[0, 5, 10, 15])
     check(wl, chains=[0, 15], mode=hy.TREE, label="c3_tree")
