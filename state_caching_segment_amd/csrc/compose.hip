@@ -640,9 +640,15 @@ k_compose_lean(TreeArgs targ) {
             const int64_t sb = sb_at(j);
             float *o_first = a.o + ((int64_t)e * a.w * a.n_chains + chain) * dk;
             if (sb >= 0 && seam_one_stage) {
-                // (staged during the previous staging phase)
+                // (staged during the previous staging phase)  The window is a
+                // dependent chain; the other workgroup's waves on the SIMD are
+                // mostly in their product or staging, so the window goes first
+                // at issue: 1.281-1.289 against 1.298-1.308 ms on 960 GDN
+                // chains (d = 128, 48 entries) in the same calls.
+                __builtin_amdgcn_s_setprio(1);
                 seam_chunk_bf16<D, FAM>(X, sm, a.w, o_first, (int64_t)a.n_chains * dk, c0, dk, seam_nm[wv][0],
                                         seam_nm[wv][1]);
+                __builtin_amdgcn_s_setprio(0);
                 // the window's output stores complete before S_j is requested
                 // (the memory counter is counted in issue order): 1.321-1.323
                 // against 1.338-1.343 ms on 960 GDN chains (d = 128, 48
