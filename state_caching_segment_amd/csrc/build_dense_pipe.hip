@@ -507,8 +507,9 @@ k_build_dense_pipe(BuildArgs a) {
         // Y = [0 | E V] - lambda Z, split.  Y and the block solve are a
         // dependent chain: a carry wave in them goes first at issue on its
         // SIMD (11.63-11.83 against 11.69-11.90 ms for 960 GDN chains of a
-        // 32k-token request, six same-call comparisons).
-        if constexpr (!PF) __builtin_amdgcn_s_setprio(1);
+        // 32k-token request, six same-call comparisons; the prefill 19.50-19.53
+        // against 19.61-19.66 ms).
+        __builtin_amdgcn_s_setprio(1);
         s4 Yh[4][2], Yl[4][2];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
@@ -554,7 +555,7 @@ k_build_dense_pipe(BuildArgs a) {
             prefill_out<D, Cfg>(QS, Rh, Rl, buf, a, b0 + (int64_t)c * CH, (int)(n - (int64_t)c * CH), chain,
                                    16 * wv - 16);
         }
-        if constexpr (!PF) __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_s_setprio(0);
         // X = lambda X + K^T R'
         if (FAM == GDN) {
 #pragma unroll
