@@ -72,7 +72,10 @@ struct PipeCfg {
     static constexpr int offB = 2 * BUF;
     static constexpr int offN = offB + CH * 4;
     static constexpr int offI = offN + 4 * 16 * LDT * 4;
-    static constexpr int total = offI + 4 * TILE * 2;
+    // (PF) the chunk whose K and Q rows the factor wave has stored: the gate
+    // wave forms tril(Q K^T) from them
+    static constexpr int offFlag = offI + 4 * TILE * 2;
+    static constexpr int total = offFlag + 16;
     static_assert(total <= 160 * 1024, "LDS budget");
 };
 
@@ -209,6 +212,10 @@ k_build_dense_pipe(BuildArgs a) {
     const int64_t b0 = a.seg_begin[seg], n = a.seg_end[seg] - b0;
     const int nch = (int)((n + CH - 1) / CH);
 
+    if constexpr (PF) {
+        if (tid == 0) *reinterpret_cast<int *>(smem + Cfg::offFlag) = -1;
+        __syncthreads();
+    }
     // Carry waves and factor waves run separate loops that meet at the same
     // number of barriers: (nch > 0) + nch.
     if (wv >= NC) {
@@ -282,6 +289,40 @@ k_build_dense_pipe(BuildArgs a) {
                         for (int e = 0; e < 8; ++e) bV[(8 * p + e) * LDV + lane] = ec * (float)pre[p][e];
                 }
                 if (lane == 0) *reinterpret_cast<float *>(buf + Cfg::bLam) = __builtin_amdgcn_exp2f(gc);
+                if constexpr (PF) {
+                    // the lower blocks of tril(Q K^T), once the factor wave
+                    // has stored this chunk's K and Q rows (a bounded wait:
+                    // the factor wave sets the flag early in its step).  On
+                    // the factor wave they set the prefill's period: 19.6
+                    // against 16.7 ms without them.
+                    const volatile int *vf = reinterpret_cast<const volatile int *>(smem + Cfg::offFlag);
+                    for (int it = 0; it < (1 << 20) && *vf != c; ++it) __builtin_amdgcn_s_sleep(1);
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+                    const bf16 *bK = reinterpret_cast<const bf16 *>(buf + Cfg::bK);
+                    // block (tb, ib <= tb) of tril(Q K^T) as the A operand: the lane
+                    // needs (Q K^T)[16 tb + r16][16 ib + 4 grp + e], which is where
+                    // the C layout of K_ib Q_tb^T puts it (exact: bf16 products
+                    // summed in fp32), split hi + lo
+                    const bf16 *bQ = reinterpret_cast<const bf16 *>(buf + Cfg::bQ);
+                    bf16 *bQK = reinterpret_cast<bf16 *>(buf + Cfg::bQK);
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+                        for (int ib = 0; ib <= tb; ++ib) {
+                            f32x4 cq = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int kb = 0; kb < KB; ++kb)
+                                cq = mfma(lds_cont(bK, LDK, 16 * ib + r16, 32 * kb, grp),
+                                          lds_cont(bQ, LDK, 16 * tb + r16, 32 * kb, grp), cq);
+                            if (ib == tb) {
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) cq[e] = (4 * grp + e <= r16) ? cq[e] : 0.f;
+                            }
+                            tile_put(bQK + (tb * (tb + 1) / 2 + ib) * TILE, r16, grp, cq);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
                 return;
             }
             bf16 *bK = reinterpret_cast<bf16 *>(buf + Cfg::bK);
@@ -316,29 +357,10 @@ k_build_dense_pipe(BuildArgs a) {
             }
             wave_lds_fence();
             if constexpr (PF) {
-                // block (tb, ib <= tb) of tril(Q K^T) as the A operand: the lane
-                // needs (Q K^T)[16 tb + r16][16 ib + 4 grp + e], which is where
-                // the C layout of K_ib Q_tb^T puts it (exact: bf16 products
-                // summed in fp32), split hi + lo
-                const bf16 *bQ = reinterpret_cast<const bf16 *>(buf + Cfg::bQ);
-                bf16 *bQK = reinterpret_cast<bf16 *>(buf + Cfg::bQK);
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb) {
-#pragma unroll
-                    for (int ib = 0; ib <= tb; ++ib) {
-                        f32x4 cq = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int kb = 0; kb < KB; ++kb)
-                            cq = mfma(lds_cont(bK, LDK, 16 * ib + r16, 32 * kb, grp),
-                                      lds_cont(bQ, LDK, 16 * tb + r16, 32 * kb, grp), cq);
-                        if (ib == tb) {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) cq[e] = (4 * grp + e <= r16) ? cq[e] : 0.f;
-                        }
-                        tile_put(bQK + (tb * (tb + 1) / 2 + ib) * TILE, r16, grp, cq);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+                // K and Q rows of chunk c are in place: the gate wave takes
+                // tril(Q K^T) from here
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+                if (lane == 0) *reinterpret_cast<volatile int *>(smem + Cfg::offFlag) = c;
             }
             // Gram tiles, one block row b at a time, in C layout: the lane holds
             // rows t = 16b + 4grp + e, column i = 16c + r16 of N0 = beta_t G_ti.
