@@ -25,7 +25,9 @@
 //     block per lane group) and forms A_b and M_bc, written pre-split into
 //     hi + lo bf16 in the layout the carry waves read as MFMA A operands.
 //   factor wave 1: scans the gates (DPP) and stages E V of the next chunk in
-//     fp32, transposed, so an S wave reads its Y tile in one 16-byte load.
+//     fp32, transposed, so an S wave reads its Y tile in one 16-byte load
+//     (prefill: then forms the lower blocks of tril(Q K^T) once factor wave
+//     0 has flagged the chunk's K and Q rows in LDS).
 // Each factor wave works alone, so its steps need no workgroup barrier.
 // Chunk inputs are prefetched two chunks ahead into the factor waves'
 // registers; the factors live in a double-buffered LDS area; the workgroup
