@@ -283,3 +283,31 @@ def test_variant_calls_validation():
         expect(-4, cw, L, x, 16, 4, 1, 1, 8, 8, 16, 16, 16)
     finally:
         del os.environ["HYPIC_FAULT_INJECT"]
+
+
+def test_compact_pair_validation():
+    """hypic_pair_compact and hypic_compose_compact refuse what they cannot
+    run, and misaligned pointers, before any launch; with aligned stand-in
+    pointers the checks pass and the fault-injection switch stops the call."""
+    L = hy.layout("gdn", "bf16", 4, 128)
+    pc, cc = hy.hypic_pair_compact, hy.hypic_compose_compact
+    expect(-2, pc, hy.layout("gla", "bf16", 4, 128), 2, P, P, P)               # diagonal T
+    expect(-1, pc, L, -1, P, P, P)                                             # n_slots < 0
+    expect(-1, pc, L, 2, None, P, P)                                           # NULL T
+    expect(-1, pc, L, 2, P + 8, P, P)                                          # T not 16-byte aligned
+    expect(-1, pc, L, 2, P, P + 4, P)                                          # compact T not 8-byte aligned
+    pc(L, 0, None, None, None)                                                 # nothing to do
+    expect(-2, cc, hy.layout("kda", "bf16", 4, 128), 1, 2, P, P, 2, P, P, P, None, None, 0, P, None)
+    expect(-2, cc, hy.layout("gdn", "f32", 4, 128), 1, 2, P, P, 2, P, P, P, None, None, 0, P, None)
+    expect(-1, cc, L, 1, 2, P, P, 2, None, P, P, None, None, 0, P, None)      # NULL compact T
+    expect(-1, cc, L, 1, 2, P, P, 2, P + 4, P, P, None, None, 0, P, None)     # compact T misaligned
+    expect(-1, cc, L, 1, 2, P, P, 2, P, P, P + 8, None, None, 0, P, None)     # S misaligned
+    expect(-1, cc, L, 1, 2, P, P, 2, P, P, P, None, None, 0, P + 2, None)     # state misaligned
+    x = _fake_tokens("gdn", cs=128)
+    expect(-1, cc, L, 1, 2, P, P, 2, P, P, P, x, P, 8, P, None)               # seams without outputs
+    os.environ["HYPIC_FAULT_INJECT"] = "all"
+    try:
+        expect(-4, pc, L, 2, P, P, P)
+        expect(-4, cc, L, 1, 2, P, P, 2, P, P, P, x, P, 8, P, P)
+    finally:
+        del os.environ["HYPIC_FAULT_INJECT"]
